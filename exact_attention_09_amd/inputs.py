@@ -1,0 +1,96 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
+
+This module holds none of the attention arithmetic: it only draws q, k, v and rounds them to the
+storage format the kernel reads. Both the HIP path and the CPU oracle are fed from here.
+
+Recipe (the workloads the pages describe; no dataset is involved):
+  * q [B, Nq, Hq, D], then k [B, Nk, Hkv, D], then v [B, Nk, Hkv, D], drawn in that order as iid
+    N(0, 1) fp32 from ``torch.Generator("cpu").manual_seed(seed)``;
+  * fp16 / bf16: round-to-nearest-even cast of the fp32 draw;
+  * fp8 e4m3 (OCP "fn" variant): per-tensor scale s = amax|x| / 448, codes = cast(clamp(x / s, +-448))
+    with round-to-nearest-even; the dequantisation scale handed to the kernel is s. The clamp is
+    needed because the cast maps values past the largest finite code to NaN instead of saturating.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+E4M3_MAX = 448.0
+
+
+def draw_qkv(B, Nq, Nk, Hq, Hkv, D, seed):
+    """fp32 CPU tensors q, k, v drawn iid N(0, 1) in the order q, k, v."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    q = torch.randn(B, Nq, Hq, D, generator=g)
+    k = torch.randn(B, Nk, Hkv, D, generator=g)
+    v = torch.randn(B, Nk, Hkv, D, generator=g)
+    return q, k, v
+
+
+def quantize_e4m3(x: torch.Tensor):
+    """Per-tensor e4m3 quantisation: returns (codes as torch.float8_e4m3fn, dequant scale float)."""
+    amax = float(x.abs().max())
+    s = amax / E4M3_MAX if amax > 0 else 1.0
+    s = float(torch.tensor(s, dtype=torch.float32))          # the scale is an fp32 number
+    x8 = (x / s).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+    return x8, s
+
+
+def to_storage(q, k, v, dtype: str):
+    """Round fp32 q, k, v to the kernel's storage type. Returns (q, k, v, descale) with
+    descale = (sq, sk, sv) for e4m3 and None otherwise."""
+    if dtype == "f16":
+        return q.half(), k.half(), v.half(), None
+    if dtype == "bf16":
+        return q.bfloat16(), k.bfloat16(), v.bfloat16(), None
+    if dtype == "e4m3":
+        (q8, sq), (k8, sk), (v8, sv) = quantize_e4m3(q), quantize_e4m3(k), quantize_e4m3(v)
+        return q8, k8, v8, (sq, sk, sv)
+    raise ValueError(f"unknown dtype {dtype}")
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One attention forward problem: sizes, storage type, mask and scale (None = 1/sqrt(D))."""
+    name: str
+    B: int
+    Nq: int
+    Nk: int
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: str
+    causal: bool = False
+    window: tuple = (-1, -1)
+    scale: float | None = None
+    seeds: tuple = field(default=(0,))
+
+    def softmax_scale(self) -> float:
+        return self.scale if self.scale is not None else self.D ** -0.5
+
+
+# The workloads the pages use, in the [batch, seqlen, nheads, headdim] layout.
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("mha_b1_h2_n128_d64_f16", 1, 128, 128, 2, 2, 64, "f16", seeds=(0, 1, 2)),
+        Workload("mha_b2_h8_n512_d64_f16", 2, 512, 512, 8, 8, 64, "f16", scale=0.125, seeds=(0, 1, 2)),
+        Workload("causal_b4_h32_n4096_d64_f16", 4, 4096, 4096, 32, 32, 64, "f16", causal=True, scale=0.125),
+        Workload("causal_b4_h32_n4096_d64_bf16", 4, 4096, 4096, 32, 32, 64, "bf16", causal=True, scale=0.125),
+        Workload("gqa_b1_hq32_hkv8_n16384_d128_bf16", 1, 16384, 16384, 32, 8, 128, "bf16", causal=True),
+        Workload("mqa_b1_hq32_hkv1_n16384_d128_bf16", 1, 16384, 16384, 32, 1, 128, "bf16", causal=True),
+        Workload("gqa_win256_b1_hq32_hkv8_n16384_d128_bf16", 1, 16384, 16384, 32, 8, 128, "bf16", causal=True,
+                 window=(256, 256)),
+        Workload("mqa_win256_b1_hq32_hkv1_n16384_d128_bf16", 1, 16384, 16384, 32, 1, 128, "bf16", causal=True,
+                 window=(256, 256)),
+        Workload("causal_fp8_b2_h32_n4096_d64_e4m3", 2, 4096, 4096, 32, 32, 64, "e4m3", causal=True, scale=0.125),
+    ]
+}
+
+
+def make_inputs(w: Workload, seed: int):
+    """(q, k, v, descale) for workload ``w`` on the CPU, in storage format."""
+    q, k, v = draw_qkv(w.B, w.Nq, w.Nk, w.Hq, w.Hkv, w.D, seed)
+    return to_storage(q, k, v, w.dtype)
