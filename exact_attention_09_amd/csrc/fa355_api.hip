@@ -1,0 +1,199 @@
+// fa355_api.hip — the C ABI of libfa355: argument validation, launch planning and dispatch.
+//
+// The entry point follows the pages' interface ("Flash Attention - Fast Memory-Efficient
+// Attention", skill page, Workflow 2 Steps 2-3: q, k, v in [batch, seqlen, nheads, headdim],
+// causal, window_size = (left, right), softmax_scale, fewer K/V heads; Workflow 3: fp8 e4m3
+// inputs). Every argument is checked here, before any device call; nothing is allocated.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa355.h"
+#include "fa_kernels.hpp"
+#include "fa_mask.hpp"
+
+namespace fa {
+hipError_t launch_fwd_f16(const FwdArgs& a, int D, int dtype, int64_t grid, hipStream_t stream);
+hipError_t launch_fwd_fp8(const FwdArgs& a, int D, int64_t grid, hipStream_t stream);
+
+TileShape tile_shape(int D, int dtype) {
+  (void)D;
+  (void)dtype;
+  TileShape t;
+  t.waves = 4;
+  t.block_m = 32 * t.waves;
+  t.block_n = 64;
+  const int es = dtype == FA_FP8_E4M3 ? 1 : 2;
+  t.lds_bytes = 2 * 2 * t.block_n * D * es;
+  return t;
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, int64_t grid, hipStream_t stream) {
+  if (dtype == FA_FP8_E4M3) return launch_fwd_fp8(a, D, grid, stream);
+  return launch_fwd_f16(a, D, dtype, grid, stream);
+}
+}  // namespace fa
+
+namespace {
+
+constexpr int kMaxSeq = 1 << 30;
+constexpr int64_t kMaxSpan = (int64_t)1 << 31;
+constexpr int kSpanSlack = 256;  // rows a tile may reach past the end of a sequence
+
+bool finite_pos(float x) { return isfinite(x) && x > 0.f; }
+
+int elem_bytes(int dtype) { return dtype == FA_FP8_E4M3 ? 1 : 2; }
+
+fa_status check_sizes(int B, int Nq, int Nk, int Hq, int Hkv, int D, int wl, int wr, int dtype) {
+  if (dtype != FA_F16 && dtype != FA_BF16 && dtype != FA_FP8_E4M3) return FA_ERR_DTYPE;
+  if (B < 1 || Nq < 1 || Nk < 1 || Hq < 1 || Hkv < 1) return FA_ERR_SHAPE;
+  if (Nq > kMaxSeq || Nk > kMaxSeq || Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  if (wl < -1 || wr < -1) return FA_ERR_WINDOW;
+  const fa::TileShape ts = fa::tile_shape(D, dtype);
+  const int64_t tiles = ((int64_t)Nq + ts.block_m - 1) / ts.block_m;
+  if ((int64_t)B * Hq * tiles >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+// Bytes one head of a tensor spans (rows 0..n-1) and the check that a tile reaching kSpanSlack
+// rows past the end still addresses it with 32-bit offsets.
+bool span_ok(int64_t n, int64_t row_stride, int D, int es, uint32_t* bytes) {
+  const int64_t span = ((n - 1) * row_stride + D) * es;
+  const int64_t reach = ((n + kSpanSlack) * row_stride + D) * es;
+  if (span >= kMaxSpan || reach >= kMaxSpan) return false;
+  *bytes = (uint32_t)span;
+  return true;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_version(void) { return 100; }
+
+const char* fa_status_str(fa_status s) {
+  switch (s) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid sizes (B, Nq, Nk, Hq, Hkv >= 1, Hq % Hkv == 0, sizes <= 2^30)";
+    case FA_ERR_HEAD_DIM: return "head dimension must be 64 or 128";
+    case FA_ERR_WINDOW: return "window bounds must be -1 (unbounded) or >= 0";
+    case FA_ERR_SCALE: return "softmax_scale and descales must be finite and > 0";
+    case FA_ERR_STRIDES: return "invalid strides or alignment (16-byte aligned, rows must not overlap)";
+    case FA_ERR_DTYPE: return "unknown dtype";
+    case FA_ERR_DESCALE: return "fp8 e4m3 needs descale_qkv";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_TOO_LARGE: return "one head of a tensor spans 2^31 bytes or more";
+  }
+  return "unknown status";
+}
+
+fa_status fa_kv_tile_range(int Nq, int Nk, int causal, int window_left, int window_right, int block_n,
+                           int row_begin, int row_end, int* tile_begin, int* tile_end, int* full, int* partial,
+                           int* skipped) {
+  if (!tile_begin || !tile_end) return FA_ERR_NULL;
+  if (Nq < 1 || Nk < 1 || Nq > kMaxSeq || Nk > kMaxSeq || block_n < 1) return FA_ERR_SHAPE;
+  if (row_begin < 0 || row_end > Nq || row_begin >= row_end) return FA_ERR_SHAPE;
+  if (window_left < -1 || window_right < -1) return FA_ERR_WINDOW;
+  const fa::MaskSpec ms{Nq, Nk, causal ? 1 : 0, window_left, window_right};
+  fa::tile_range(ms, row_begin, row_end - 1, block_n, tile_begin, tile_end);
+  int nf = 0, np = 0, ns = 0;
+  for (int t = *tile_begin; t < *tile_end; ++t) {
+    const int c = fa::classify_tile(ms, row_begin, row_end - 1, t * block_n, block_n);
+    nf += c == fa::TILE_FULL;
+    np += c == fa::TILE_PARTIAL;
+    ns += c == fa::TILE_SKIP;
+  }
+  if (full) *full = nf;
+  if (partial) *partial = np;
+  if (skipped) *skipped = ns;
+  return FA_OK;
+}
+
+fa_status fa_fwd_plan(int B, int Nq, int Nk, int Hq, int Hkv, int D, int causal, int window_left, int window_right,
+                      fa_dtype dtype, fa_plan_info* info) {
+  if (!info) return FA_ERR_NULL;
+  const fa_status st = check_sizes(B, Nq, Nk, Hq, Hkv, D, window_left, window_right, dtype);
+  if (st != FA_OK) return st;
+  const fa::TileShape ts = fa::tile_shape(D, dtype);
+  info->block_m = ts.block_m;
+  info->block_n = ts.block_n;
+  info->waves = ts.waves;
+  info->num_q_tiles = (Nq + ts.block_m - 1) / ts.block_m;
+  info->grid = (int64_t)B * Hq * info->num_q_tiles;
+  info->lds_bytes = ts.lds_bytes;
+  const fa::MaskSpec ms{Nq, Nk, causal ? 1 : 0, window_left, window_right};
+  int64_t tiles = 0;
+  for (int qt = 0; qt < info->num_q_tiles; ++qt) {
+    int tb, te;
+    const int r0 = qt * ts.block_m, r1 = (r0 + ts.block_m < Nq ? r0 + ts.block_m : Nq) - 1;
+    fa::tile_range(ms, r0, r1, ts.block_n, &tb, &te);
+    tiles += te - tb;
+  }
+  info->kv_tiles = tiles * B * Hq;
+  return FA_OK;
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Nq, int Nk, int Hq,
+                 int Hkv, int D, const fa_strides* s, float softmax_scale, int causal, int window_left,
+                 int window_right, fa_dtype dtype, hipStream_t stream, const float* descale_qkv) {
+  if (!q || !k || !v || !out || !s) return FA_ERR_NULL;
+  fa_status st = check_sizes(B, Nq, Nk, Hq, Hkv, D, window_left, window_right, dtype);
+  if (st != FA_OK) return st;
+  if (!finite_pos(softmax_scale)) return FA_ERR_SCALE;
+  float dq = 1.f, dk = 1.f, dv = 1.f;
+  if (dtype == FA_FP8_E4M3) {
+    if (!descale_qkv) return FA_ERR_DESCALE;
+    dq = descale_qkv[0];
+    dk = descale_qkv[1];
+    dv = descale_qkv[2];
+    if (!finite_pos(dq) || !finite_pos(dk) || !finite_pos(dv)) return FA_ERR_SCALE;
+  }
+  const int es = elem_bytes(dtype);
+  const int oes = 2;
+  // strides: non-negative; output rows and heads must not overlap; 16-byte alignment
+  const int64_t in_str[9] = {s->q_b, s->q_n, s->q_h, s->k_b, s->k_n, s->k_h, s->v_b, s->v_n, s->v_h};
+  for (int i = 0; i < 9; ++i)
+    if (in_str[i] < 0 || (in_str[i] * es) % 16 != 0) return FA_ERR_STRIDES;
+  const int64_t out_str[3] = {s->o_b, s->o_n, s->o_h};
+  for (int i = 0; i < 3; ++i)
+    if (out_str[i] < 0 || (out_str[i] * oes) % 16 != 0) return FA_ERR_STRIDES;
+  if ((Nq > 1 && s->o_n < D) || (Hq > 1 && s->o_h < D) || (B > 1 && s->o_b < D)) return FA_ERR_STRIDES;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || ((uintptr_t)lse & 3u)) return FA_ERR_STRIDES;
+
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = out;
+  a.lse = lse;
+  a.B = B;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.group = Hq / Hkv;
+  a.causal = causal ? 1 : 0;
+  a.wl = window_left;
+  a.wr = window_right;
+  a.q_b = s->q_b; a.q_n = s->q_n; a.q_h = s->q_h;
+  a.k_b = s->k_b; a.k_n = s->k_n; a.k_h = s->k_h;
+  a.v_b = s->v_b; a.v_n = s->v_n; a.v_h = s->v_h;
+  a.o_b = s->o_b; a.o_n = s->o_n; a.o_h = s->o_h;
+  if (!span_ok(Nq, s->q_n, D, es, &a.q_bytes) || !span_ok(Nk, s->k_n, D, es, &a.k_bytes) ||
+      !span_ok(Nk, s->v_n, D, es, &a.v_bytes) || !span_ok(Nq, s->o_n, D, oes, &a.o_bytes))
+    return FA_ERR_TOO_LARGE;
+  const double log2e = 1.4426950408889634074;
+  a.scale_log2 = (float)((double)softmax_scale * dq * dk * log2e);
+  a.out_scale = dtype == FA_FP8_E4M3 ? dv / 256.f : 1.f;
+  const fa::TileShape ts = fa::tile_shape(D, dtype);
+  a.num_q_tiles = (Nq + ts.block_m - 1) / ts.block_m;
+  const int64_t grid = (int64_t)B * Hq * a.num_q_tiles;
+  const hipError_t e = fa::launch_fwd(a, D, dtype, grid, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // extern "C"

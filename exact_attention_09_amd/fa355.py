@@ -1,0 +1,150 @@
+"""Python binding of libfa355 (ctypes): argument marshalling only.
+
+Every step of the attention forward pass runs in the HIP kernels behind ``fa_fwd``; this module
+only allocates the outputs with PyTorch, reads tensor strides and the current HIP stream, and
+calls the C ABI declared in ``include/fa355.h``. There is no fallback: if the library is missing
+or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa355.so")
+
+FA_F16, FA_BF16, FA_FP8_E4M3 = 0, 1, 2
+_DTYPE_CODE = {torch.float16: FA_F16, torch.bfloat16: FA_BF16, torch.float8_e4m3fn: FA_FP8_E4M3}
+_OUT_DTYPE = {FA_F16: torch.float16, FA_BF16: torch.bfloat16, FA_FP8_E4M3: torch.bfloat16}
+
+# Every symbol include/fa355.h declares.
+EXPORTED = ("fa_fwd", "fa_status_str", "fa_fwd_plan", "fa_kv_tile_range", "fa_version")
+
+
+class FaStrides(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in
+                ("q_b", "q_n", "q_h", "k_b", "k_n", "k_h", "v_b", "v_n", "v_h", "o_b", "o_n", "o_h")]
+
+
+class FaPlanInfo(ctypes.Structure):
+    _fields_ = [("block_m", ctypes.c_int), ("block_n", ctypes.c_int), ("waves", ctypes.c_int),
+                ("num_q_tiles", ctypes.c_int), ("grid", ctypes.c_int64), ("lds_bytes", ctypes.c_int),
+                ("kv_tiles", ctypes.c_int64)]
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"fa_fwd failed: status {status}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa355.so from the package directory (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m exact_attention_09_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    c_int, c_float, c_void_p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+    lib.fa_fwd.restype = c_int
+    lib.fa_fwd.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                           c_int, c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(FaStrides),
+                           c_float, c_int, c_int, c_int, c_int, c_void_p, ctypes.POINTER(c_float)]
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_status_str.argtypes = [c_int]
+    lib.fa_fwd_plan.restype = c_int
+    lib.fa_fwd_plan.argtypes = [c_int] * 10 + [ctypes.POINTER(FaPlanInfo)]
+    lib.fa_kv_tile_range.restype = c_int
+    lib.fa_kv_tile_range.argtypes = [c_int] * 8 + [ctypes.POINTER(c_int)] * 5
+    lib.fa_version.restype = c_int
+    lib.fa_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().fa_status_str(int(status)).decode()
+
+
+def _strides(q, k, v, o) -> FaStrides:
+    s = FaStrides()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if t.stride(3) != 1:
+            raise ValueError(f"{name}: the head dimension must be contiguous (stride 1), got {t.stride()}")
+        setattr(s, name + "_b", t.stride(0))
+        setattr(s, name + "_n", t.stride(1))
+        setattr(s, name + "_h", t.stride(2))
+    return s
+
+
+def fwd_raw(q, k, v, out, lse, causal=False, window=(-1, -1), softmax_scale=None, descale=None,
+            stream=None) -> int:
+    """Call fa_fwd on caller-provided tensors; returns the status code (0 = ok) without raising."""
+    lib = load()
+    code = _DTYPE_CODE.get(q.dtype)
+    if code is None:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    B, Nq, Hq, D = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    scale = float(D) ** -0.5 if softmax_scale is None else float(softmax_scale)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    desc = None
+    if descale is not None:
+        desc = (ctypes.c_float * 3)(*[float(x) for x in descale])
+    st = _strides(q, k, v, out)
+    return lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                      lse.data_ptr() if lse is not None else None,
+                      B, Nq, Nk, Hq, Hkv, D, ctypes.byref(st), scale, int(bool(causal)),
+                      int(window[0]), int(window[1]), code, stream, desc)
+
+
+def fwd(q, k, v, causal=False, window=(-1, -1), softmax_scale=None, descale=None, return_lse=True,
+        out=None, lse=None):
+    """FlashAttention forward on the GPU.
+
+    q: [B, Nq, Hq, D]; k, v: [B, Nk, Hkv, D], all fp16, all bf16, or all float8_e4m3fn (then
+    ``descale=(dq, dk, dv)`` is required). ``softmax_scale=None`` means 1/sqrt(D).
+    Returns (out [B, Nq, Hq, D], lse [B, Hq, Nq] fp32 or None).
+    """
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share one dtype")
+    code = _DTYPE_CODE.get(q.dtype)
+    if code is None:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    B, Nq, Hq, D = q.shape
+    if out is None:
+        out = torch.empty(B, Nq, Hq, D, dtype=_OUT_DTYPE[code], device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty(B, Hq, Nq, dtype=torch.float32, device=q.device)
+    status = fwd_raw(q, k, v, out, lse, causal, window, softmax_scale, descale)
+    if status != 0:
+        raise FaError(status, status_str(status))
+    return out, lse
+
+
+def plan(B, Nq, Nk, Hq, Hkv, D, causal=False, window=(-1, -1), dtype=FA_F16) -> dict:
+    info = FaPlanInfo()
+    st = load().fa_fwd_plan(B, Nq, Nk, Hq, Hkv, D, int(bool(causal)), int(window[0]), int(window[1]), int(dtype),
+                            ctypes.byref(info))
+    if st != 0:
+        raise FaError(st, status_str(st))
+    return {f: getattr(info, f) for f, _ in FaPlanInfo._fields_}
+
+
+def kv_tile_range(Nq, Nk, causal, window, block_n, row_begin, row_end):
+    """(tile_begin, tile_end, full, partial, skipped) for query rows [row_begin, row_end)."""
+    vals = [ctypes.c_int() for _ in range(5)]
+    st = load().fa_kv_tile_range(Nq, Nk, int(bool(causal)), int(window[0]), int(window[1]), block_n, row_begin,
+                                 row_end, *[ctypes.byref(x) for x in vals])
+    if st != 0:
+        raise FaError(st, status_str(st))
+    return tuple(x.value for x in vals)

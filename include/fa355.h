@@ -1,0 +1,136 @@
+/*
+ * fa355.h — C ABI of libfa355: the FlashAttention forward pass on AMD MI355X (gfx950).
+ *
+ * What is computed ("Flash Attention - Fast Memory-Efficient Attention", skill page, Workflow 1
+ * Step 2 and Workflow 2 Steps 2-3; "What FlashAttention is and how it speeds up attention",
+ * sections 1-3: the fused, blocked computation is exact):
+ *
+ *   out[b, i, h, :] = sum_j softmax_j(s_ij) * v[b, j, g, :],
+ *   s_ij = softmax_scale * <q[b, i, h, :], k[b, j, g, :]>,   g = h / (Hq / Hkv)
+ *   lse[b, h, i]    = ln sum_j exp(s_ij)        (over admitted keys j only)
+ *
+ * in one fused kernel with an online softmax: the Nq x Nk score matrix is never written to
+ * device memory. Key j is admitted for query row i when, with off = Nk - Nq,
+ *   0 <= j < Nk,
+ *   causal == 0 or j <= i + off                (bottom-right alignment; the usual lower
+ *                                               triangle when Nq == Nk),
+ *   window_left  < 0 or j >= i + off - window_left,
+ *   window_right < 0 or j <= i + off + window_right.
+ * A row with no admitted key gets out = 0 and lse = -inf.
+ *
+ * Tensors use the pages' [batch, seqlen, nheads, headdim] layout (skill page, Quick start and
+ * Workflow 2 Step 2) with arbitrary element strides for batch, seqlen and heads; headdim is
+ * contiguous. K and V may have fewer heads than Q (MQA / GQA, skill page, Workflow 2 Step 3):
+ * query head h reads K/V head h / (Hq / Hkv).
+ *
+ * Storage types (skill page, Workflow 3 for fp8):
+ *   FA_F16       q, k, v, out: IEEE binary16.
+ *   FA_BF16      q, k, v, out: bfloat16.
+ *   FA_FP8_E4M3  q, k, v: OCP fp8 E4M3 codes (max 448, no infinities) with per-tensor
+ *                dequantisation scales; out: bfloat16. The score is
+ *                softmax_scale * (dq * q8) . (dk * k8) and the output is sum_j p_ij * (dv * v8).
+ * Arithmetic: fp32 accumulation of both products and of the softmax statistics.
+ */
+#ifndef FA355_H
+#define FA355_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_dtype {
+  FA_F16 = 0,
+  FA_BF16 = 1,
+  FA_FP8_E4M3 = 2
+} fa_dtype;
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,      /* q, k, v, out or strides is NULL (lse may be NULL)                      */
+  FA_ERR_SHAPE = 2,     /* B, Nq, Nk, Hq or Hkv < 1, Hq % Hkv != 0, or a size above 2^30          */
+  FA_ERR_HEAD_DIM = 3,  /* D is not 64 or 128                                                      */
+  FA_ERR_WINDOW = 4,    /* window_left or window_right < -1                                       */
+  FA_ERR_SCALE = 5,     /* softmax_scale not finite and > 0, or a descale not finite and > 0      */
+  FA_ERR_STRIDES = 6,   /* a stride < 0, rows overlap (seqlen stride < D or head stride < D),     */
+                        /* or a pointer / stride not 16-byte aligned                              */
+  FA_ERR_DTYPE = 7,     /* unknown dtype                                                           */
+  FA_ERR_DESCALE = 8,   /* FA_FP8_E4M3 without descale_qkv                                         */
+  FA_ERR_LAUNCH = 9,    /* the kernel launch failed (HIP error; e.g. no device)                    */
+  FA_ERR_TOO_LARGE = 10 /* one head's span of q, k, v or out reaches 2^31 bytes                    */
+} fa_status;
+
+/* Element strides (not bytes) of the batch, seqlen and head axes; the headdim stride is 1. */
+typedef struct fa_strides {
+  int64_t q_b, q_n, q_h;
+  int64_t k_b, k_n, k_h;
+  int64_t v_b, v_n, v_h;
+  int64_t o_b, o_n, o_h;
+} fa_strides;
+
+/*
+ * fa_fwd — enqueue one attention forward pass on `stream`.
+ *
+ * q    device, [B, Nq, Hq, D] in `dtype` storage.
+ * k, v device, [B, Nk, Hkv, D] in `dtype` storage.
+ * out  device, [B, Nq, Hq, D]: fp16 for FA_F16, bf16 for FA_BF16 and FA_FP8_E4M3. Must not
+ *      alias q, k or v.
+ * lse  device fp32 [B, Hq, Nq], contiguous, natural log, scale (and fp8 descales) included;
+ *      may be NULL, then it is not written.
+ * softmax_scale  finite, > 0 (callers wanting the default pass 1/sqrt(D)).
+ * causal         0 or 1.  window_left / window_right: -1 = unbounded, else >= 0.
+ * descale_qkv    host float[3] = {dq, dk, dv}; required for FA_FP8_E4M3, ignored otherwise.
+ * stream         HIP stream (0 = the null stream).
+ *
+ * Ownership: the caller allocates and owns every buffer. The library allocates no device
+ * memory, keeps no per-call state, and is reentrant. The call is asynchronous: it returns once
+ * the kernel is enqueued and never synchronises. Arguments are validated before any device call;
+ * an invalid call returns its error code and touches nothing. Faults inside the kernel surface as
+ * HIP errors at the caller's next synchronisation.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                 int B, int Nq, int Nk, int Hq, int Hkv, int D, const fa_strides* strides,
+                 float softmax_scale, int causal, int window_left, int window_right,
+                 fa_dtype dtype, hipStream_t stream, const float* descale_qkv);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fa_status_str(fa_status s);
+
+/* Launch plan of one fa_fwd call (host only, no device call). */
+typedef struct fa_plan_info {
+  int block_m;        /* query rows per workgroup                                   */
+  int block_n;        /* keys per K/V tile                                          */
+  int waves;          /* wavefronts per workgroup                                   */
+  int num_q_tiles;    /* ceil(Nq / block_m)                                         */
+  int64_t grid;       /* workgroups launched = B * Hq * num_q_tiles                 */
+  int lds_bytes;      /* LDS per workgroup                                          */
+  int64_t kv_tiles;   /* K/V tiles visited, summed over all workgroups              */
+} fa_plan_info;
+
+/*
+ * fa_fwd_plan — the plan fa_fwd would launch for these sizes and options, computed on the host.
+ * Same validation rules as fa_fwd for the arguments it takes. Returns FA_OK and fills *info.
+ */
+fa_status fa_fwd_plan(int B, int Nq, int Nk, int Hq, int Hkv, int D, int causal, int window_left,
+                      int window_right, fa_dtype dtype, fa_plan_info* info);
+
+/*
+ * fa_kv_tile_range — for query rows [row_begin, row_end) the K/V tiles of `block_n` keys that
+ * hold at least one admitted key lie in [*tile_begin, *tile_end) (empty when equal). For the
+ * rows [row_begin, row_end) and tile t, *full / *partial / *skipped (each may be NULL) count the
+ * tiles in that range that are admitted for every pair, for some pairs, and for none. Host only.
+ */
+fa_status fa_kv_tile_range(int Nq, int Nk, int causal, int window_left, int window_right,
+                           int block_n, int row_begin, int row_end, int* tile_begin, int* tile_end,
+                           int* full, int* partial, int* skipped);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA355_H */

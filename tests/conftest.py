@@ -25,3 +25,13 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    # Name each GPU case on the real stderr before it runs, so a run that dies inside a kernel
+    # still says which case it was in.
+    if "gpu" in request.node.keywords:
+        sys.__stderr__.write(f"[gpu-case] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield
