@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark of the FlashAttention forward pass (libfa355) on one MI355X.
+
+One step = one fa_fwd call over one batch of the workload (the whole hot path: a single fused
+kernel). Default workload: causal attention, B=4, Hq=Hkv=32, Nq=Nk=4096, D=64, fp16, scale 1/8 —
+the pages' benchmark shape ("Flash Attention - Fast Memory-Efficient Attention", skill page,
+Workflow 2 Step 4, [4, 4096, 32, 64] fp16, 10 warm-up and 100 timed iterations), run causal.
+
+Metric: attention forward TFLOP/s with FLOPs = 4 * B * Hq * Nq * Nk * D, halved for causal; for
+a sliding window the admitted-pair count replaces Nq * Nk (4 * B * Hq * D * pairs). Inputs are
+resident in device memory before the timed region. Prints one JSON line.
+
+Also reported:
+  * roofline — the kernel's achieved TFLOP/s against MI355X's dense MFMA peak for its dtype,
+    from HIP events recorded around each launch on the launch stream; HBM traffic from the
+    committed rocprofv3 counter summary when it was taken on the current kernel source;
+  * cpu_baseline — the fp64 CPU oracle timed on this host on a bounded sample of the same
+    workload (whole heads), scaled to the same metric.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "e4m3": 5033.2}   # 256 CU x 2.4 GHz x dense MFMA rate
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "causal_b4_h32_n4096_d64_f16"
+METRIC = "attention fwd TFLOP/s (4·B·H·Nq·Nk·D, causal halved) and % of MFMA peak"
+KERNEL_SOURCES = ["exact_attention_09_amd/csrc/fa_fwd_f16.hip", "exact_attention_09_amd/csrc/fa_fwd_fp8.hip",
+                  "exact_attention_09_amd/csrc/fa_mask.hpp", "exact_attention_09_amd/csrc/fa_kernels.hpp",
+                  "exact_attention_09_amd/csrc/fa355_api.hip"]
+
+
+def admitted_pairs(Nq, Nk, causal, window):
+    """Number of admitted (query, key) pairs, by rows (closed-form interval per row)."""
+    off = Nk - Nq
+    wl, wr = window
+    right = 0 if causal else wr
+    total = 0
+    for i in range(Nq):
+        lo = 0 if wl < 0 else max(0, i + off - wl)
+        hi = Nk - 1 if right < 0 else min(Nk - 1, i + off + right)
+        total += max(0, hi - lo + 1)
+    return total
+
+
+def metric_flops(w):
+    """Metric FLOPs of one forward pass of workload w."""
+    if w.window == (-1, -1):
+        f = 4.0 * w.B * w.Hq * w.Nq * w.Nk * w.D
+        return f / 2 if w.causal else f
+    return 4.0 * w.B * w.Hq * w.D * admitted_pairs(w.Nq, w.Nk, w.causal, w.window)
+
+
+def algorithmic_bytes(w):
+    """Bytes the pass must move at least: q, k, v read once, out and lse written once."""
+    es = 1 if w.dtype == "e4m3" else 2
+    return (w.B * w.Nq * w.Hq * w.D * es + 2 * w.B * w.Nk * w.Hkv * w.D * es + w.B * w.Nq * w.Hq * w.D * 2
+            + w.B * w.Hq * w.Nq * 4)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload):
+    """HBM bytes per launch from the committed counter summary, if taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, descale, budget_s):
+    """Time the fp64 oracle on whole heads of the same inputs until budget_s has passed."""
+    import numpy as np
+
+    from oracle import attention_fp64, decode_bf16_bits, decode_e4m3_codes, decode_f16_bits
+
+    def dec(x, s):
+        import torch
+        x = x.contiguous()
+        if x.dtype == torch.float16:
+            return decode_f16_bits(x.view(torch.int16).numpy().view(np.uint16))
+        if x.dtype == torch.bfloat16:
+            return decode_bf16_bits(x.view(torch.int16).numpy().view(np.uint16))
+        return decode_e4m3_codes(x.view(torch.uint8).numpy(), s)
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max((i.get("num_threads", 1) for i in blas), default=1)
+        blas_name = ",".join(sorted({i.get("internal_api", "?") for i in blas})) or "unknown"
+    except Exception:  # pragma: no cover
+        threads, blas_name = 1, "unknown"
+    dq, dk, dv = descale if descale is not None else (1.0, 1.0, 1.0)
+    G = w.Hq // w.Hkv
+    heads = 0
+    t0 = time.perf_counter()
+    elapsed = 0.0
+    for b in range(w.B):
+        for h in range(w.Hq):
+            g = h // G
+            qh = dec(q[b:b + 1, :, h:h + 1, :], dq)
+            kh = dec(k[b:b + 1, :, g:g + 1, :], dk)
+            vh = dec(v[b:b + 1, :, g:g + 1, :], dv)
+            attention_fp64(qh, kh, vh, w.softmax_scale(), w.causal, w.window)
+            heads += 1
+            elapsed = time.perf_counter() - t0
+            if elapsed >= budget_s:
+                break
+        if elapsed >= budget_s:
+            break
+    per_head_flops = metric_flops(w) / (w.B * w.Hq)
+    return {
+        "value": heads * per_head_flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{heads} of {w.B * w.Hq} (batch, head) pairs of the same inputs, full fp64 score matrix per "
+                  f"head, {elapsed:.1f} s wall; metric FLOPs of those heads / wall time; BLAS={blas_name} "
+                  f"threads={threads}, host logical CPUs={os.cpu_count()}",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
+                    help="oracle time budget on the host; 0 skips the CPU baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of attention, run a plain device copy of MIB MiB (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs are not part of this "
+                                   "build (the forward pass shards by (batch, head) with no exchange)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    import exact_attention_09_amd as fa
+    from exact_attention_09_amd.inputs import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        x = torch.ones(n, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(args.warmup + args.steps):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                          "launches": args.warmup + args.steps}))
+        return
+
+    w = WORKLOADS[args.workload]
+    seed = w.seeds[0]
+    q, k, v, descale = make_inputs(w, seed)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    out = torch.empty(w.B, w.Nq, w.Hq, w.D, dtype=torch.float16 if w.dtype == "f16" else torch.bfloat16,
+                      device=dev)
+    lse = torch.empty(w.B, w.Hq, w.Nq, dtype=torch.float32, device=dev)
+    scale = w.softmax_scale()
+
+    def step():
+        st = fa.fwd_raw(qd, kd, vd, out, lse, w.causal, w.window, scale, descale)
+        if st != 0:
+            raise fa.FaError(st, fa.status_str(st))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)     # fa_fwd launches on this stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_kernel_s = sum(kernel_ms) / len(kernel_ms) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+
+    flops = metric_flops(w)
+    value = flops / (ms_per_step / 1e3) / 1e12
+    achieved = flops / avg_kernel_s / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = committed_traffic(w.name)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Nq": w.Nq, "Nk": w.Nk, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+                   "causal": w.causal, "window": list(w.window), "softmax_scale": scale, "seed": seed,
+                   "metric_flops": flops},
+        "pct_of_mfma_peak": round(100.0 * value / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel_avg_us": round(avg_kernel_s * 1e6, 3),
+                     "algorithmic_bytes": algorithmic_bytes(w),
+                     "algorithmic_GBps": round(algorithmic_bytes(w) / avg_kernel_s / 1e9, 1)},
+    }
+    if args.cpu_baseline_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, descale, args.cpu_baseline_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -28,6 +28,8 @@ FLAGS = [
     "-Wno-unused-function",
     # Packed fp32 VALU ops are kept out of the generated code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the softmax reads and rescales them with VALU ops.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

@@ -21,10 +21,12 @@
 //    holds are a permutation of 8 consecutive MFMA k-slots, and V^T is read in the same
 //    permuted key order with ds_read_b64_tr_b16 (LDS transpose read), so P never leaves
 //    registers.
-//  * K and V tiles (BN keys) are double-buffered in LDS: tile t+1 is fetched from HBM with
-//    128-bit buffer loads while tile t is computed, then written to the other buffer. K rows are
-//    XOR-swizzled by (row & 7) in 16-byte chunks and V rows by 2 * (row & 3), which keeps the
-//    128-bit K reads and the transpose reads of V free of bank conflicts.
+//  * K and V tiles (BN keys) stream HBM -> LDS with 128-bit buffer loads that write LDS directly
+//    (no register staging), into three-slot rings: while tile t is computed, the loads of K(t+3)
+//    and V(t+2) are in flight, so each load has two iterations to land. Each lane's 16 bytes land
+//    at its own slot position; which global chunk a lane fetches implements the LDS swizzle.
+//  * S of tile t+1 is computed while tile t goes through the softmax and the PV product (K runs
+//    one tile ahead of V), so the MFMAs of one overlap the VALU work of the other.
 //  * Softmax in base 2: t = s * (scale * log2 e); p = exp2(t - m); alpha = exp2(m_old - m_new).
 //  * Tiles with no admitted key are skipped; tiles admitted for every pair run without a mask;
 //    only partial tiles (the causal diagonal, window edges, the ragged end) are masked.
@@ -60,6 +62,11 @@ struct F16 {
   __device__ static inline uint32_t pack(float x, float y) {
     return __builtin_bit_cast(uint32_t, f16x2{(_Float16)x, (_Float16)y});
   }
+  // Row-sum contribution of a packed pair: the fp16-rounded p values the PV product uses,
+  // summed in fp32 (v_dot2c_f32_f16 against (1, 1)).
+  __device__ static inline float sum2(float acc, uint32_t packed, float, float) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), f16x2{(_Float16)1.f, (_Float16)1.f}, acc, false);
+  }
 };
 
 struct BF16 {
@@ -71,6 +78,8 @@ struct BF16 {
   __device__ static inline uint32_t pack(float x, float y) {
     return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)x, (__bf16)y});
   }
+  // bf16 rounding of p is too coarse for a 1e-3 lse: the row sum uses the fp32 values.
+  __device__ static inline float sum2(float acc, uint32_t, float x, float y) { return acc + (x + y); }
 };
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -94,6 +103,58 @@ __device__ inline float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Softmax reference. p = exp2(s * c - m) is computed against the row's current reference m
+// without first taking the tile's row max. If every p of the tile is at most 2^15 (checked
+// through the row sum, which bounds each term), the tile is done: the products and sums use the
+// same m as the final division and the lse, so the result is unchanged, and p stays inside the
+// fp16 range. Otherwise (the first tile of a row, where m = -inf, or a score far above every
+// earlier one) the wave takes the slow path: m moves to the running max, O and l are rescaled
+// by exp2(m_old - m_new), and p is recomputed.
+constexpr float kSumBound = 32768.f;
+
+// LDS bank model of gfx950: 64 banks of 4 bytes, a 128-bit read served 16 lanes (256 bytes) per
+// cycle. Swizzles below are XORs on the 16-byte chunk index of a row; they make
+//  * the K reads (16 consecutive rows, one chunk each) hit 16 distinct 16-byte bank groups,
+//  * the V transpose reads (4 rows x 64 bytes per 32 lanes) hit distinct bank groups,
+//  * the row-major tile writes stay conflict-free (a row's chunks are only permuted).
+template <int ROWB>
+__device__ inline int k_swz(int row) {
+  return ROWB == 128 ? (row >> 1) & 7 : row & 15;
+}
+template <int ROWB>
+__device__ inline int v_swz(int row) {
+  return ROWB == 128 ? (row & 3) << 1 : (row & 3) << 2;
+}
+
+// One 16-byte-per-lane HBM -> LDS load (buffer_load_dwordx4 ... lds): lane l's 16 bytes land at
+// LDS byte address lds_addr + 16 * l. Written out here rather than through the compiler's
+// builtin because the compiler's wait-count pass, unable to tell LDS ring slots apart, would put a
+// blanket vmcnt(0) in front of the V transpose reads and undo the prefetch. The kernel waits for
+// these loads itself (vmcnt before each barrier). There is no destination register: nothing in the
+// register file is left pending. M0 is written by this block (declared clobbered); the s_nop is
+// the wait state between a write of M0 and its use by the load.
+struct BufDesc {
+  uint32_t w[4];
+};
+__device__ inline BufDesc make_desc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return BufDesc{{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, kRsrcWord3}};
+}
+__device__ inline void dma16(const BufDesc& d, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 rs = u32x4{d.w[0], d.w[1], d.w[2], d.w[3]};
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, %3 offen lds"
+      :
+      : "v"(voff), "s"(rs), "s"(lds_addr), "s"(soff)
+      : "memory", "m0");
+}
+__device__ inline uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 template <class TR, int D, int BN, int WAVES>
 __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   constexpr int NT = WAVES * 64;        // threads per workgroup
@@ -107,9 +168,12 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   constexpr int DB = D / 32;            // 32-wide column blocks of the output
   constexpr int KS = D / 16;            // MFMA k-steps over the head dimension
   static_assert(BN * CPR % NT == 0, "tile must split evenly over the workgroup");
-  static_assert(CPR >= 8, "swizzles need at least 8 chunks per row");
+  static_assert(ROWB == 128 || ROWB == 256, "swizzles are laid out for 128- or 256-byte rows");
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILEB];  // [stage][K | V][BN][D]
+  constexpr int NS = 3;                 // ring slots per tensor
+  __shared__ __attribute__((aligned(16))) char smem[2 * NS * TILEB];  // [K0 K1 K2 | V0 V1 V2]
+  char* const kring = smem;
+  char* const vring = smem + NS * TILEB;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -134,8 +198,6 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   const char* vbp = (const char*)a.v + (b * a.v_b + hk * a.v_h) * ES;
   char* ob = (char*)a.o + (b * a.o_b + h * a.o_h) * ES;
   const __amdgpu_buffer_rsrc_t q_r = make_rsrc(qb, a.q_bytes);
-  const __amdgpu_buffer_rsrc_t k_r = make_rsrc(kbp, a.k_bytes);
-  const __amdgpu_buffer_rsrc_t v_r = make_rsrc(vbp, a.v_bytes);
   const __amdgpu_buffer_rsrc_t o_r = make_rsrc(ob, a.o_bytes);
   const uint32_t q_rowb = (uint32_t)(a.q_n * ES), k_rowb = (uint32_t)(a.k_n * ES);
   const uint32_t v_rowb = (uint32_t)(a.v_n * ES), o_rowb = (uint32_t)(a.o_n * ES);
@@ -147,9 +209,19 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   const int w0 = q0 + wave * 32;
   const bool wave_live = w0 < a.Nq;
   const int w1 = min(w0 + 31, a.Nq - 1);
+  // Key bounds of the wave's first and last rows, clamped to [-1, Nk] (wave-uniform scalars):
+  // a tile is skipped if it ends before lo(w0) or starts after hi(w1), and needs no mask if it
+  // lies inside [lo(w1), hi(w0)].
+  auto clamp_key = [&](int64_t x) { return (int)(x < -1 ? -1 : (x > a.Nk ? a.Nk : x)); };
+  const int wlo0 = __builtin_amdgcn_readfirstlane(clamp_key(key_lo(ms, w0)));
+  const int wlo1 = __builtin_amdgcn_readfirstlane(clamp_key(key_lo(ms, w1)));
+  const int whi0 = __builtin_amdgcn_readfirstlane(clamp_key(key_hi(ms, w0)));
+  const int whi1 = __builtin_amdgcn_readfirstlane(clamp_key(key_hi(ms, w1)));
+  auto tile_live = [&](int t) { return wave_live && t * BN + BN - 1 >= wlo0 && t * BN <= whi1; };
+  auto tile_partial = [&](int t) { return !(wlo1 <= t * BN && t * BN + BN - 1 <= whi0); };
   const int my_row = w0 + l32;
-  const int lo_i = (int)key_lo(ms, my_row);
-  const int hi_i = (int)key_hi(ms, my_row);
+  const int lo_i = clamp_key(key_lo(ms, my_row));
+  const int hi_i = clamp_key(key_hi(ms, my_row));
   const uint32_t span_i = hi_i >= lo_i ? (uint32_t)(hi_i - lo_i + 1) : 0u;
 
   // ---- Q operands (B operand of S^T): row my_row, head-dim slots ks*16 + hl*8 .. +7
@@ -157,33 +229,42 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
     qop[ks] = __builtin_amdgcn_raw_buffer_load_b128(q_r, (uint32_t)my_row * q_rowb + (ks * 16 + hl * 8) * ES, 0, 0);
+  // Q must have landed before the pipelined loop: without this wait the compiler's wait-count
+  // analysis, merging the loop back edge, would make every iteration wait on the prefetches.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
-  // ---- global -> register -> LDS staging of one K/V tile
-  i32x4 kreg[CH], vreg[CH];
-  auto gload = [&](int t) {
-    const int j0 = t * BN;
+  // ---- HBM -> LDS loads of one K or V tile. Load i of a thread writes the 16 bytes at slot
+  // position P = (i * NT + tid) * 16; P holds row P / ROWB, physical chunk (P % ROWB) / 16, i.e.
+  // logical chunk physical ^ swizzle(row). Rows past the end read as 0 (buffer bounds).
+  uint32_t kgoff[CH], vgoff[CH];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + i * NT, row = c / CPR, cc = c % CPR;
-      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(k_r, (uint32_t)(j0 + row) * k_rowb + cc * 16, 0, 0);
-      vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(v_r, (uint32_t)(j0 + row) * v_rowb + cc * 16, 0, 0);
-    }
+  for (int i = 0; i < CH; ++i) {
+    const int pos = (i * NT + tid) * 16, row = pos / ROWB, pc = (pos % ROWB) / 16;
+    kgoff[i] = (uint32_t)row * k_rowb + ((pc ^ k_swz<ROWB>(row)) << 4);
+    vgoff[i] = (uint32_t)row * v_rowb + ((pc ^ v_swz<ROWB>(row)) << 4);
+  }
+  const BufDesc k_d = make_desc(kbp, a.k_bytes), v_d = make_desc(vbp, a.v_bytes);
+  auto dma = [&](const BufDesc& d, const uint32_t* goff, uint32_t rowb, int t, char* slot) {
+    const uint32_t base = (uint32_t)(t * BN) * rowb;
+    const uint32_t lds = lds_addr_of(slot) + wave * 64 * 16;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) dma16(d, goff[i], base, lds + i * NT * 16);
   };
-  auto lstore = [&](int st) {
-    char* ks = smem + st * 2 * TILEB;
-    char* vs = ks + TILEB;
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int c = tid + i * NT, row = c / CPR, cc = c % CPR;
-      *(i32x4*)(ks + row * ROWB + ((cc ^ (row & 7)) << 4)) = kreg[i];
-      *(i32x4*)(vs + row * ROWB + ((cc ^ ((row & 3) << 1)) << 4)) = vreg[i];
-    }
+  // Barrier that waits only for this thread's loads older than the newest `pending` ones: a
+  // compiler-only fence keeps LDS accesses on their side, and no blanket vmcnt(0) is emitted.
+  auto barrier_keep = [&](int pending) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (pending >= 2 * CH) __builtin_amdgcn_s_waitcnt(0x0070 | (2 * CH));   // vmcnt(2CH) lgkmcnt(0)
+    else if (pending >= CH) __builtin_amdgcn_s_waitcnt(0x0070 | CH);       // vmcnt(CH)  lgkmcnt(0)
+    else __builtin_amdgcn_s_waitcnt(0x0070);                               // vmcnt(0)   lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
 
-  // Per-lane LDS offsets. K (A operand of S^T): row kb*32 + l32, chunk (2*ks + hl) ^ (l32 & 7).
+  // Per-lane LDS offsets. K (A operand of S^T): row kb*32 + l32, chunk 2*ks + hl.
   int koff[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) koff[ks] = l32 * ROWB + (((2 * ks + hl) ^ (l32 & 7)) << 4);
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = l32 * ROWB + (((2 * ks + hl) ^ k_swz<ROWB>(l32)) << 4);
   // V (A operand of O^T, transpose read): within each 16-lane group g, source lane 4t + c reads
   // row 4*(g>>1) + t (+8 for the second read), columns db*32 + (g&1)*16 + 4c .. +3.
   const int g16 = lane >> 4, s16 = lane & 15, tr = s16 >> 2, tc = s16 & 3;
@@ -191,78 +272,115 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
     const int chunk = db * 4 + (g16 & 1) * 2 + (tc >> 1);
-    voff[db] = (4 * (g16 >> 1) + tr) * ROWB + ((chunk ^ (tr << 1)) << 4) + (tc & 1) * 8;
+    voff[db] = (4 * (g16 >> 1) + tr) * ROWB + ((chunk ^ v_swz<ROWB>(tr)) << 4) + (tc & 1) * 8;
   }
 
+  auto compute_s = [&](const char* ks, f32x16* s) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      i32x4 kop[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) kop[kb] = *(const i32x4*)(ks + kb * 32 * ROWB + koff[k]);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) s[kb] = TR::mfma(kop[kb], qop[k], s[kb]);
+    }
+  };
+
   const float c2 = a.scale_log2;
-  float m = -INFINITY;   // running max of score * c2 for this lane's query
+  float m = -INFINITY;   // reference max of score * c2 for this lane's query
   float l = 0.f;         // this lane's share of the running sum (lanes l, l^32 split the keys)
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
 
+  // ---- pipeline fill: K(tb), V(tb), K(tb+1) landed; S(tb); V(tb+1), K(tb+2) in flight
   if (tb < te) {
-    gload(tb);
-    lstore(0);
+    dma(k_d, kgoff, k_rowb, tb, kring);
+    dma(v_d, vgoff, v_rowb, tb, vring);
+    if (tb + 1 < te) dma(k_d, kgoff, k_rowb, tb + 1, kring + TILEB);
   }
-  __syncthreads();
+  barrier_keep(0);
+  f32x16 sa[KB], sb[KB];
+  if (tb < te && tile_live(tb)) compute_s(kring, sa);
+  if (tb + 1 < te) dma(v_d, vgoff, v_rowb, tb + 1, vring + TILEB);
+  if (tb + 2 < te) dma(k_d, kgoff, k_rowb, tb + 2, kring + 2 * TILEB);
+  barrier_keep(2 * CH);    // K(tb) fully read by every wave before its slot is reused
 
-  for (int t = tb; t < te; ++t) {
-    const int st = (t - tb) & 1;
-    if (t + 1 < te) gload(t + 1);
-    const int j0 = t * BN;
-    const int cls = wave_live ? classify_tile(ms, w0, w1, j0, BN) : TILE_SKIP;
-    if (cls != TILE_SKIP) {
-      const char* ks = smem + st * 2 * TILEB;
-      const char* vs = ks + TILEB;
-      // S^T = K Q^T
-      f32x16 s[KB];
+  // One pipeline step: S(t+1) into sn while tile t (scores in sc) goes through the softmax and
+  // the PV product. Two steps per loop trip swap the roles of the two S arrays.
+  auto step = [&](int t, f32x16 (&sc)[KB], f32x16 (&sn)[KB]) {
+    const int i = t - tb;
+    const int s0 = i % NS, s1 = (i + 1) % NS, s2 = (i + 2) % NS;   // ring slots of tiles t, t+1, t+2
+    const bool k3 = t + 3 < te, v2 = t + 2 < te;
+    // K(t+3) into K(t)'s slot (read last step); V(t+2) into V(t-1)'s slot (read last step)
+    if (k3) dma(k_d, kgoff, k_rowb, t + 3, kring + s0 * TILEB);
+    if (v2) dma(v_d, vgoff, v_rowb, t + 2, vring + s2 * TILEB);
+    if (t + 1 < te && tile_live(t + 1)) compute_s(kring + s1 * TILEB, sn);
+    if (tile_live(t)) {
+      const int j0 = t * BN;
+      // V^T operands for this tile
+      i32x4 vop[KB][2][DB];
+      {
+        const char* vs = vring + s0 * TILEB;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int k = 0; k < KS; ++k) {
+          for (int half = 0; half < 2; ++half)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const i32x4 kop = *(const i32x4*)(ks + kb * 32 * ROWB + koff[k]);
-          s[kb] = TR::mfma(kop, qop[k], s[kb]);
-        }
+            for (int db = 0; db < DB; ++db) {
+              const char* p = vs + (kb * 32 + half * 16) * ROWB + voff[db];
+              const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+              const i16x4 v1r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * ROWB));
+              vop[kb][half][db] = i32x4{__builtin_bit_cast(i32x2, v0)[0], __builtin_bit_cast(i32x2, v0)[1],
+                                        __builtin_bit_cast(i32x2, v1r)[0], __builtin_bit_cast(i32x2, v1r)[1]};
+            }
       }
-      // mask: key of accumulator r in block kb is j0 + kb*32 + (r/4)*8 + hl*4 + r%4
-      if (cls == TILE_PARTIAL) {
+      // mask (partial tiles only): key of accumulator r in block kb is j0 + kb*32 + (r/4)*8 + hl*4 + r%4
+      if (tile_partial(t)) {
         const int jl = j0 + hl * 4 - lo_i;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int j = jl + kb * 32 + (r >> 2) * 8 + (r & 3);
-            if ((uint32_t)j >= span_i) s[kb][r] = -INFINITY;
+            sc[kb][r] = (uint32_t)j < span_i ? sc[kb][r] : -INFINITY;
           }
       }
-      // online softmax (base 2)
-      float mx = s[0][0];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      mx = pair_max(mx);
-      const float m_new = fmaxf(m, mx * c2);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-      float rs = 0.f;
+      // p = exp2(s * c - m), packed to the MFMA type, and the row sum
       uint32_t pk[KB][8];
+      float rs;
+      auto exponentiate = [&](float mref) {
+        rs = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c2, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], c2, -m_use));
-          rs += p0 + p1;
-          pk[kb][r >> 1] = TR::pack(p0, p1);
-        }
-      l = l * alpha + rs;
-      m = m_new;
+          for (int r = 0; r < 16; r += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], c2, -mref));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r + 1], c2, -mref));
+            pk[kb][r >> 1] = TR::pack(p0, p1);
+            rs = TR::sum2(rs, pk[kb][r >> 1], p0, p1);
+          }
+      };
+      exponentiate(m);
+      if (__builtin_amdgcn_ballot_w64(!(rs <= kSumBound))) {
+        // slow path: move the reference to the running max, rescale, recompute
+        float mx = sc[0][0];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+        const float m_new = fmaxf(m, pair_max(mx) * c2);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        m = m_new;
+        exponentiate(m_use);
+      }
+      l += rs;
       // O^T += V^T P^T
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -271,18 +389,16 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
           const i32x4 pop = i32x4{(int)pk[kb][4 * half + 0], (int)pk[kb][4 * half + 1], (int)pk[kb][4 * half + 2],
                                   (int)pk[kb][4 * half + 3]};
 #pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const char* p = vs + (kb * 32 + half * 16) * ROWB + voff[db];
-            const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-            const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * ROWB));
-            const i32x4 vop = i32x4{__builtin_bit_cast(i32x2, v0)[0], __builtin_bit_cast(i32x2, v0)[1],
-                                    __builtin_bit_cast(i32x2, v1)[0], __builtin_bit_cast(i32x2, v1)[1]};
-            o[db] = TR::mfma(vop, pop, o[db]);
-          }
+          for (int db = 0; db < DB; ++db) o[db] = TR::mfma(vop[kb][half][db], pop, o[db]);
         }
     }
-    if (t + 1 < te) lstore(st ^ 1);
-    __syncthreads();
+    // K(t+2) and V(t+1) must have landed for the next step; this step's loads stay in flight
+    barrier_keep(CH * ((int)k3 + (int)v2));
+  };
+
+  for (int t = tb; t < te; t += 2) {
+    step(t, sa, sb);
+    if (t + 1 < te) step(t + 1, sb, sa);
   }
 
   // ---- epilogue: O / l, lse = (m + log2 l) * ln 2
