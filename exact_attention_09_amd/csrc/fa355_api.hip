@@ -24,7 +24,7 @@ TileShape tile_shape(int D, int dtype) {
   t.block_m = 32 * t.waves;
   t.block_n = 64;
   const int es = dtype == FA_FP8_E4M3 ? 1 : 2;
-  t.lds_bytes = 2 * 2 * t.block_n * D * es;
+  t.lds_bytes = 2 * 3 * t.block_n * D * es;   // three-slot K and V rings
   return t;
 }
 
@@ -188,7 +188,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* out, float* 
     return FA_ERR_TOO_LARGE;
   const double log2e = 1.4426950408889634074;
   a.scale_log2 = (float)((double)softmax_scale * dq * dk * log2e);
-  a.out_scale = dtype == FA_FP8_E4M3 ? dv / 256.f : 1.f;
+  a.out_scale = dtype == FA_FP8_E4M3 ? dv : 1.f;
   const fa::TileShape ts = fa::tile_shape(D, dtype);
   a.num_q_tiles = (Nq + ts.block_m - 1) / ts.block_m;
   const int64_t grid = (int64_t)B * Hq * a.num_q_tiles;

@@ -35,23 +35,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_device.hpp"
 #include "fa_kernels.hpp"
 #include "fa_mask.hpp"
 
 namespace fa {
-
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9 family)
-constexpr float kLn2 = 0.69314718055994530942f;
 
 struct F16 {
   static constexpr int kDtype = 0;
@@ -82,27 +70,6 @@ struct BF16 {
   __device__ static inline float sum2(float acc, uint32_t, float x, float y) { return acc + (x + y); }
 };
 
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
-}
-
-// Block index -> logical block index, so that each XCD's share is one contiguous range.
-__device__ inline int xcd_remap(int id, int n) {
-  const int xcd = id & 7, k = id >> 3;
-  const int per = n >> 3, rem = n & 7;
-  return xcd * per + (xcd < rem ? xcd : rem) + k;
-}
-
-// Value of x held by lane l ^ 32, combined with x: max or sum over the lane pair.
-__device__ inline float pair_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ inline float pair_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
 // Softmax reference. p = exp2(s * c - m) is computed against the row's current reference m
 // without first taking the tile's row max. If every p of the tile is at most 2^15 (checked
 // through the row sum, which bounds each term), the tile is done: the products and sums use the
@@ -124,35 +91,6 @@ __device__ inline int k_swz(int row) {
 template <int ROWB>
 __device__ inline int v_swz(int row) {
   return ROWB == 128 ? (row & 3) << 1 : (row & 3) << 2;
-}
-
-// One 16-byte-per-lane HBM -> LDS load (buffer_load_dwordx4 ... lds): lane l's 16 bytes land at
-// LDS byte address lds_addr + 16 * l. Written out here rather than through the compiler's
-// builtin because the compiler's wait-count pass, unable to tell LDS ring slots apart, would put a
-// blanket vmcnt(0) in front of the V transpose reads and undo the prefetch. The kernel waits for
-// these loads itself (vmcnt before each barrier). There is no destination register: nothing in the
-// register file is left pending. M0 is written by this block (declared clobbered); the s_nop is
-// the wait state between a write of M0 and its use by the load.
-struct BufDesc {
-  uint32_t w[4];
-};
-__device__ inline BufDesc make_desc(const void* base, uint32_t bytes) {
-  const uint64_t a = (uint64_t)(uintptr_t)base;
-  return BufDesc{{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, kRsrcWord3}};
-}
-__device__ inline void dma16(const BufDesc& d, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 rs = u32x4{d.w[0], d.w[1], d.w[2], d.w[3]};
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %0, %1, %3 offen lds"
-      :
-      : "v"(voff), "s"(rs), "s"(lds_addr), "s"(soff)
-      : "memory", "m0");
-}
-__device__ inline uint32_t lds_addr_of(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
 template <class TR, int D, int BN, int WAVES>

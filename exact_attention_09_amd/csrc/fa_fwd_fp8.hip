@@ -1,8 +1,317 @@
-// fa_fwd_fp8.hip — FlashAttention forward for fp8 e4m3 storage on gfx950 (placeholder).
+// fa_fwd_fp8.hip — FlashAttention forward for fp8 e4m3 storage on gfx950 (MI355X).
+//
+// Same method and pipeline as the fp16/bf16 kernel (blocks of Q, K, V in on-chip memory, online
+// softmax with a running renormalisation, one fused kernel: "What FlashAttention is and how it
+// speeds up attention", sections 1-2), for the pages' fp8 inputs ("Flash Attention - Fast
+// Memory-Efficient Attention", skill page, Workflow 3: q, k, v cast to float8_e4m3). q, k, v are
+// e4m3 codes with per-tensor dequantisation scales dq, dk, dv; the score is
+// softmax_scale * dq * dk * <q8, k8> and the output sum_j p_ij * dv * v8_j, written as bf16.
+//
+// CDNA4 mapping (differences from the 16-bit kernel):
+//  * Both products run on v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3, fp32 accumulate): a lane
+//    holds 32 consecutive k-slots, so one MFMA covers 64 head-dim values of S^T = K Q^T, and one
+//    covers 64 keys of O^T = V^T P^T.
+//  * P is rounded to e4m3 after a 2^8 shift that keeps small weights above the format's
+//    subnormal range. To keep p * 2^8 <= 448 (the largest e4m3 value), the row reference m moves
+//    whenever a tile's row max exceeds it by more than 0.8 (log2 units): p <= 2^0.8. The running
+//    sum (and so the lse) uses the unrounded fp32 p.
+//  * V^T is read with ds_read_b64_tr_b8: a lane receives 8 consecutive LDS rows of one column.
+//    The 16 keys a lane half holds in the S^T accumulator (keys g*8 + half*4 + e, g, e < 4, of
+//    each 32-key block) are stored as 16 consecutive LDS rows (row half*16 + g*4 + e): the HBM ->
+//    LDS loads pick the global row of each LDS row, so this permutation costs nothing.
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
+#include "fa_device.hpp"
 #include "fa_kernels.hpp"
+#include "fa_mask.hpp"
 
 namespace fa {
-hipError_t launch_fwd_fp8(const FwdArgs&, int, int64_t, hipStream_t) { return hipErrorNotSupported; }
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+// log2 of the 2^8 shift applied to p before its e4m3 rounding, and the reference threshold.
+constexpr float kPShiftLog2 = 8.0f;
+constexpr float kTau8 = 0.8f;
+
+// 64-bank LDS swizzles (16-byte chunk XOR) for 64- and 128-byte rows.
+template <int ROWB>
+__device__ inline int k_swz8(int row) {
+  return ROWB == 64 ? (row >> 2) & 3 : (row >> 1) & 7;
+}
+template <int ROWB>
+__device__ inline int v_swz8(int row) {
+  return ROWB == 64 ? ((row >> 2) & 1) << 1 : ((row >> 1) & 3) << 1;
+}
+// Key (within the tile) stored at LDS row rho of a V tile.
+__device__ inline int v_key_of_row(int rho) {
+  return (rho & ~31) | (((rho >> 2) & 3) << 3) | (((rho >> 4) & 1) << 2) | (rho & 3);
+}
+
+__device__ inline f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+template <int D, int BN, int WAVES>
+__global__ void __launch_bounds__(WAVES * 64) fa_fwd_fp8_kernel(FwdArgs a) {
+  constexpr int NT = WAVES * 64;
+  constexpr int BM = WAVES * 32;
+  constexpr int ROWB = D;               // one byte per element
+  constexpr int TILEB = BN * ROWB;
+  constexpr int CPR = ROWB / 16;        // 16-byte chunks per row
+  constexpr int CH = BN * CPR / NT;     // HBM -> LDS loads per thread per tile, per tensor
+  constexpr int KB = BN / 32;           // 32-key blocks per tile
+  constexpr int DB = D / 32;            // 32-wide output column blocks
+  constexpr int KS = D / 64;            // MFMA k-steps over the head dimension
+  constexpr int NS = 3;
+  static_assert(BN == 64, "the P operand packs two 32-key blocks into one 64-key MFMA");
+  static_assert(BN * CPR % NT == 0, "tile must split evenly over the workgroup");
+  static_assert(ROWB == 64 || ROWB == 128, "swizzles are laid out for 64- or 128-byte rows");
+
+  __shared__ __attribute__((aligned(16))) char smem[2 * NS * TILEB];  // [K0 K1 K2 | V0 V1 V2]
+  char* const kring = smem;
+  char* const vring = smem + NS * TILEB;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5;
+  const int l32 = lane & 31;
+
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = L / a.num_q_tiles;
+  int qt = L - bh * a.num_q_tiles;
+  if (a.causal) qt = a.num_q_tiles - 1 - qt;
+  const int b = bh / a.Hq;
+  const int h = bh - b * a.Hq;
+  const int hk = h / a.group;
+  const int q0 = qt * BM;
+
+  const MaskSpec ms{a.Nq, a.Nk, a.causal, a.wl, a.wr};
+
+  const char* qb = (const char*)a.q + (b * a.q_b + h * a.q_h);
+  const char* kbp = (const char*)a.k + (b * a.k_b + hk * a.k_h);
+  const char* vbp = (const char*)a.v + (b * a.v_b + hk * a.v_h);
+  char* ob = (char*)a.o + (b * a.o_b + h * a.o_h) * 2;
+  const __amdgpu_buffer_rsrc_t q_r = make_rsrc(qb, a.q_bytes);
+  const __amdgpu_buffer_rsrc_t o_r = make_rsrc(ob, a.o_bytes);
+  const uint32_t q_rowb = (uint32_t)a.q_n, k_rowb = (uint32_t)a.k_n;
+  const uint32_t v_rowb = (uint32_t)a.v_n, o_rowb = (uint32_t)(a.o_n * 2);
+
+  const int wg_last = min(q0 + BM, a.Nq) - 1;
+  int tb, te;
+  tile_range(ms, q0, wg_last, BN, &tb, &te);
+  const int w0 = q0 + wave * 32;
+  const bool wave_live = w0 < a.Nq;
+  const int w1 = min(w0 + 31, a.Nq - 1);
+  auto clamp_key = [&](int64_t x) { return (int)(x < -1 ? -1 : (x > a.Nk ? a.Nk : x)); };
+  const int wlo0 = __builtin_amdgcn_readfirstlane(clamp_key(key_lo(ms, w0)));
+  const int wlo1 = __builtin_amdgcn_readfirstlane(clamp_key(key_lo(ms, w1)));
+  const int whi0 = __builtin_amdgcn_readfirstlane(clamp_key(key_hi(ms, w0)));
+  const int whi1 = __builtin_amdgcn_readfirstlane(clamp_key(key_hi(ms, w1)));
+  auto tile_live = [&](int t) { return wave_live && t * BN + BN - 1 >= wlo0 && t * BN <= whi1; };
+  auto tile_partial = [&](int t) { return !(wlo1 <= t * BN && t * BN + BN - 1 <= whi0); };
+  const int my_row = w0 + l32;
+  const int lo_i = clamp_key(key_lo(ms, my_row));
+  const int hi_i = clamp_key(key_hi(ms, my_row));
+  const uint32_t span_i = hi_i >= lo_i ? (uint32_t)(hi_i - lo_i + 1) : 0u;
+
+  // Q operands (B operand of S^T): row my_row, head-dim bytes ks*64 + hl*32 .. +31
+  i32x8 qop[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint32_t off = (uint32_t)my_row * q_rowb + ks * 64 + hl * 32;
+    const i32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(q_r, off, 0, 0);
+    const i32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(q_r, off + 16, 0, 0);
+    qop[ks] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): Q has landed before the pipelined loop
+
+  // HBM -> LDS: slot position P = (i * NT + tid) * 16 holds LDS row P / ROWB, physical chunk
+  // (P % ROWB) / 16. K rows are in key order; V rows in the permuted order above.
+  uint32_t kgoff[CH], vgoff[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int pos = (i * NT + tid) * 16, row = pos / ROWB, pc = (pos % ROWB) / 16;
+    kgoff[i] = (uint32_t)row * k_rowb + ((pc ^ k_swz8<ROWB>(row)) << 4);
+    vgoff[i] = (uint32_t)v_key_of_row(row) * v_rowb + ((pc ^ v_swz8<ROWB>(row)) << 4);
+  }
+  const BufDesc k_d = make_desc(kbp, a.k_bytes), v_d = make_desc(vbp, a.v_bytes);
+  auto dma = [&](const BufDesc& d, const uint32_t* goff, uint32_t rowb, int t, char* slot) {
+    const uint32_t base = (uint32_t)(t * BN) * rowb;
+    const uint32_t lds = lds_addr_of(slot) + wave * 64 * 16;
+#pragma unroll
+    for (int i = 0; i < CH; ++i) dma16(d, goff[i], base, lds + i * NT * 16);
+  };
+  auto barrier_keep = [&](int pending) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (pending >= 2 * CH) __builtin_amdgcn_s_waitcnt(0x0070 | (2 * CH));
+    else if (pending >= CH) __builtin_amdgcn_s_waitcnt(0x0070 | CH);
+    else __builtin_amdgcn_s_waitcnt(0x0070);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+
+  // K (A operand of S^T): row kb*32 + l32, bytes ks*64 + hl*32 .. +31 = chunks ks*4 + hl*2 + {0,1}
+  int koff[KS][2];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int part = 0; part < 2; ++part)
+      koff[ks][part] = l32 * ROWB + (((ks * 4 + hl * 2 + part) ^ k_swz8<ROWB>(l32)) << 4);
+  // V (A operand of O^T, ds_read_b64_tr_b8): in 16-lane group g, source lane 2r + c reads LDS
+  // row (g>>1)*16 + r (+ kb*32 + part*8), bytes db*32 + (g&1)*16 + 8c .. +7.
+  const int g16 = lane >> 4, s16 = lane & 15, tr8 = s16 >> 1, tc8 = s16 & 1;
+  int voff[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const int chunk = db * 2 + (g16 & 1);
+    voff[db] = ((g16 >> 1) * 16 + tr8) * ROWB + ((chunk ^ v_swz8<ROWB>(tr8)) << 4) + tc8 * 8;
+  }
+
+  auto compute_s = [&](const char* ks, f32x16* s) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const i32x4 x0 = *(const i32x4*)(ks + kb * 32 * ROWB + koff[k][0]);
+        const i32x4 x1 = *(const i32x4*)(ks + kb * 32 * ROWB + koff[k][1]);
+        s[kb] = mfma_fp8(i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]}, qop[k], s[kb]);
+      }
+    }
+  };
+
+  const float c2 = a.scale_log2;
+  float m = -INFINITY;
+  float l = 0.f;         // sum of 2^8 * p over this lane's keys
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+
+  if (tb < te) {
+    dma(k_d, kgoff, k_rowb, tb, kring);
+    dma(v_d, vgoff, v_rowb, tb, vring);
+    if (tb + 1 < te) dma(k_d, kgoff, k_rowb, tb + 1, kring + TILEB);
+  }
+  barrier_keep(0);
+  f32x16 sa[KB], sb[KB];
+  if (tb < te && tile_live(tb)) compute_s(kring, sa);
+  if (tb + 1 < te) dma(v_d, vgoff, v_rowb, tb + 1, vring + TILEB);
+  if (tb + 2 < te) dma(k_d, kgoff, k_rowb, tb + 2, kring + 2 * TILEB);
+  barrier_keep(2 * CH);
+
+  auto step = [&](int t, f32x16 (&sc)[KB], f32x16 (&sn)[KB]) {
+    const int i = t - tb;
+    const int s0 = i % NS, s1 = (i + 1) % NS, s2 = (i + 2) % NS;
+    const bool k3 = t + 3 < te, v2 = t + 2 < te;
+    if (k3) dma(k_d, kgoff, k_rowb, t + 3, kring + s0 * TILEB);
+    if (v2) dma(v_d, vgoff, v_rowb, t + 2, vring + s2 * TILEB);
+    if (t + 1 < te && tile_live(t + 1)) compute_s(kring + s1 * TILEB, sn);
+    if (tile_live(t)) {
+      const char* vs = vring + s0 * TILEB;
+      const int j0 = t * BN;
+      // V^T operands: for each column block, 8 LDS rows per read, 4 reads = 32 keys per lane
+      i32x8 vop[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        i32x2 part[4];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr)
+            part[kb * 2 + pr] =
+                __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vs + (kb * 32 + pr * 8) * ROWB + voff[db]));
+        vop[db] = i32x8{part[0][0], part[0][1], part[1][0], part[1][1], part[2][0], part[2][1], part[3][0], part[3][1]};
+      }
+      if (tile_partial(t)) {
+        const int jl = j0 + hl * 4 - lo_i;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = jl + kb * 32 + (r >> 2) * 8 + (r & 3);
+            sc[kb][r] = (uint32_t)j < span_i ? sc[kb][r] : -INFINITY;
+          }
+      }
+      // row max, lazily moved reference (p <= 2^0.8 keeps 2^8 p inside the e4m3 range)
+      float mx = sc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+      mx = pair_max(mx) * c2;
+      const float m_new = mx > m + kTau8 ? mx : m;
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      }
+      m = m_new;
+      // 2^8 p, its fp32 sum, and its e4m3 codes in accumulator order (byte kb*16 + r)
+      const float shift = kPShiftLog2 - m_use;
+      float rs = 0.f;
+      int pw[8];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+          float p[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][4 * w4 + e], c2, shift));
+            rs += p[e];
+          }
+          int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+          pw[kb * 4 + w4] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
+        }
+      l += rs;
+      const i32x8 pop = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = mfma_fp8(vop[db], pop, o[db]);
+    }
+    barrier_keep(CH * ((int)k3 + (int)v2));
+  };
+
+  for (int t = tb; t < te; t += 2) {
+    step(t, sa, sb);
+    if (t + 1 < te) step(t + 1, sb, sa);
+  }
+
+  // epilogue: O * dv / l (both carry the 2^8 shift), lse = (m + log2(l / 2^8)) * ln 2
+  if (!wave_live || my_row >= a.Nq) return;
+  const float l_tot = pair_sum(l);
+  const float inv = l_tot > 0.f ? a.out_scale / l_tot : 0.f;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const uint32_t w0v = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)(o[db][4 * q4 + 0] * inv),
+                                                               (__bf16)(o[db][4 * q4 + 1] * inv)});
+      const uint32_t w1v = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)(o[db][4 * q4 + 2] * inv),
+                                                               (__bf16)(o[db][4 * q4 + 3] * inv)});
+      __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)w0v, (int)w1v}, o_r,
+                                            (uint32_t)my_row * o_rowb + (db * 32 + q4 * 8 + hl * 4) * 2, 0, 0);
+    }
+  if (a.lse != nullptr && hl == 0) {
+    const float lse = l_tot > 0.f ? (m - kPShiftLog2 + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+    a.lse[((int64_t)b * a.Hq + h) * a.Nq + my_row] = lse;
+  }
+}
+
+template <int D>
+static hipError_t launch_t(const FwdArgs& a, int64_t grid, hipStream_t stream) {
+  constexpr int BN = 64, WAVES = 4;
+  hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, BN, WAVES>), dim3((unsigned)grid), dim3(WAVES * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_fp8(const FwdArgs& a, int D, int64_t grid, hipStream_t stream) {
+  return D == 64 ? launch_t<64>(a, grid, stream) : launch_t<128>(a, grid, stream);
+}
+
 }  // namespace fa

@@ -22,7 +22,7 @@ struct FwdArgs {
   int64_t o_b, o_n, o_h;
   uint32_t q_bytes, k_bytes, v_bytes, o_bytes;  // one head's addressable span, in bytes
   float scale_log2;      // softmax_scale * log2(e)   (times dq * dk for fp8)
-  float out_scale;       // 1, or dv / 2^8 for fp8
+  float out_scale;       // 1, or dv for fp8
 };
 
 // Tile shapes of the launch for head dimension D and storage type.

@@ -233,3 +233,65 @@ def test_invalid_call_raises_on_device():
     with pytest.raises(fa.FaError) as e:
         fa.fwd(q, k, k)
     assert e.value.status == 2
+
+
+# ---------------------------------------------------------------- fp8 e4m3
+def test_fp8_full_size_sampled():
+    w = WORKLOADS["causal_fp8_b2_h32_n4096_d64_e4m3"]
+    q, k, v, d = make_inputs(w, w.seeds[0])
+    out, lse = fa.fwd(q.cuda(), k.cuda(), v.cuda(), w.causal, w.window, w.softmax_scale(), d)
+    torch.cuda.synchronize()
+    assert out.dtype == torch.bfloat16
+    assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(lse).all())
+    out, lse = out.cpu(), lse.cpu()
+    rng = np.random.default_rng(23)
+    # the RMS bar is taken over whole heads: compare every row of sampled heads
+    for b, h in [(0, 0), (1, 31), (int(rng.integers(0, 2)), int(rng.integers(0, 32)))]:
+        rows = np.arange(w.Nq)
+        ro, rl = oracle_rows(q, k, v, b, h, rows, w.softmax_scale(), w.causal, w.window, d)
+        compare("e4m3", out_to_f64(out[b, :, h, :]), lse[b, h].numpy().astype(np.float64), ro, rl,
+                what=f"fp8 b{b} h{h}")
+
+
+FP8_SHAPES = [
+    # B, Nq, Nk, Hq, Hkv, D, causal, window
+    (1, 128, 128, 2, 2, 64, False, (-1, -1)),
+    (2, 333, 333, 4, 2, 64, True, (-1, -1)),
+    (1, 200, 300, 4, 1, 128, False, (-1, -1)),
+    (1, 300, 300, 2, 2, 128, True, (50, 0)),
+    (1, 257, 190, 2, 1, 64, True, (-1, -1)),
+]
+
+
+@pytest.mark.parametrize("case", FP8_SHAPES, ids=lambda c: "x".join(str(x) for x in c[:6]) + f"-c{int(c[6])}-w{c[7][0]}_{c[7][1]}")
+def test_fp8_ragged_shapes(case):
+    B, Nq, Nk, Hq, Hkv, D, causal, window = case
+    q, k, v = draw_qkv(B, Nq, Nk, Hq, Hkv, D, seed=Nq + 3 * Nk)
+    q, k, v, d = to_storage(q, k, v, "e4m3")
+    full_check(q, k, v, causal, window, None, d, what=str(case))
+
+
+def test_fp8_causal_row0_is_dequantised_v0():
+    q, k, v = draw_qkv(1, 200, 200, 4, 2, 64, seed=12)
+    q, k, v, d = to_storage(q, k, v, "e4m3")
+    out, _ = run(q, k, v, causal=True, descale=d)
+    for h in range(4):
+        want = (v[0, 0, h // 2, :].float() * d[2]).bfloat16()
+        assert torch.equal(out[0, 0, h, :], want)
+
+
+@pytest.mark.parametrize("case", [(1, 4096, 4096, 2, 2, 64, True, (-1, -1)), (1, 1000, 1300, 2, 1, 128, False, (100, 31))],
+                         ids=["4096-causal", "1000x1300-win"])
+def test_fp8_mask_probe_exact(case):
+    B, Nq, Nk, Hq, Hkv, D, causal, window = case
+    for mode in (0, 1):
+        q, k, v = probe_inputs(B, Nq, Nk, Hq, Hkv, D, torch.float32, mode)
+        q, k, v = q.to(torch.float8_e4m3fn), k.clamp(-448, 448).to(torch.float8_e4m3fn), v.to(torch.float8_e4m3fn)
+        out, lse = run(q, k, v, causal, window, 1.0, descale=(1.0, 1.0, 1.0))
+        cnt, per = brute_counts(Nq, Nk, causal, window, D, mode)
+        for h in range(Hq):
+            l = lse[0, h].numpy().astype(np.float64)
+            got_cnt = np.where(np.isfinite(l), np.rint(np.exp(l)), 0).astype(np.int64)
+            assert np.array_equal(got_cnt, cnt)
+            o = out[0, :, h, :].float().numpy().astype(np.float64)
+            assert np.array_equal(np.rint(o * cnt[:, None]).astype(np.int64), per)
