@@ -34,8 +34,8 @@ HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "causal_b4_h32_n4096_d64_f16"
 METRIC = "attention fwd TFLOP/s (4·B·H·Nq·Nk·D, causal halved) and % of MFMA peak"
 KERNEL_SOURCES = ["exact_attention_09_amd/csrc/fa_fwd_f16.hip", "exact_attention_09_amd/csrc/fa_fwd_fp8.hip",
-                  "exact_attention_09_amd/csrc/fa_mask.hpp", "exact_attention_09_amd/csrc/fa_kernels.hpp",
-                  "exact_attention_09_amd/csrc/fa355_api.hip"]
+                  "exact_attention_09_amd/csrc/fa_device.hpp", "exact_attention_09_amd/csrc/fa_mask.hpp",
+                  "exact_attention_09_amd/csrc/fa_kernels.hpp", "exact_attention_09_amd/csrc/fa355_api.hip"]
 
 
 def admitted_pairs(Nq, Nk, causal, window):
@@ -76,7 +76,7 @@ def kernel_source_hash():
 
 def committed_traffic(workload):
     """HBM bytes per launch from the committed counter summary, if taken on this kernel source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
     with open(path) as f:
