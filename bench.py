@@ -33,9 +33,10 @@ PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "e4m3": 5033.2}   # 256 CU x 2.4 G
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "causal_b4_h32_n4096_d64_f16"
 METRIC = "attention fwd TFLOP/s (4·B·H·Nq·Nk·D, causal halved) and % of MFMA peak"
-KERNEL_SOURCES = ["exact_attention_09_amd/csrc/fa_fwd_f16.hip", "exact_attention_09_amd/csrc/fa_fwd_fp8.hip",
-                  "exact_attention_09_amd/csrc/fa_device.hpp", "exact_attention_09_amd/csrc/fa_mask.hpp",
-                  "exact_attention_09_amd/csrc/fa_kernels.hpp", "exact_attention_09_amd/csrc/fa355_api.hip"]
+KERNEL_SOURCES = ["exact_attention_09_amd/csrc/fa_fwd_f16.hip", "exact_attention_09_amd/csrc/fa_f16_common.hpp",
+                  "exact_attention_09_amd/csrc/fa_fwd_fp8.hip", "exact_attention_09_amd/csrc/fa_device.hpp",
+                  "exact_attention_09_amd/csrc/fa_mask.hpp", "exact_attention_09_amd/csrc/fa_kernels.hpp",
+                  "exact_attention_09_amd/csrc/fa355_api.hip"]
 
 
 def admitted_pairs(Nq, Nk, causal, window):

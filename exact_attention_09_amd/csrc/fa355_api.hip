@@ -17,14 +17,12 @@ hipError_t launch_fwd_f16(const FwdArgs& a, int D, int dtype, int64_t grid, hipS
 hipError_t launch_fwd_fp8(const FwdArgs& a, int D, int64_t grid, hipStream_t stream);
 
 TileShape tile_shape(int D, int dtype) {
-  (void)D;
-  (void)dtype;
   TileShape t;
   t.waves = 4;
   t.block_m = 32 * t.waves;
   t.block_n = 64;
   const int es = dtype == FA_FP8_E4M3 ? 1 : 2;
-  t.lds_bytes = 2 * 3 * t.block_n * D * es;   // three-slot K and V rings
+  t.lds_bytes = (3 + 3) * t.block_n * D * es;   // three-slot K and V rings
   return t;
 }
 

@@ -44,8 +44,9 @@ __device__ inline float pair_sum(float x) {
 // builtin because the compiler's wait-count pass, unable to tell LDS ring slots apart, would put a
 // blanket vmcnt(0) in front of the V transpose reads and undo the prefetch. The kernel waits for
 // these loads itself (vmcnt before each barrier). There is no destination register: nothing in the
-// register file is left pending. M0 is written by this block (declared clobbered); the s_nop is
-// the wait state between a write of M0 and its use by the load.
+// register file is left pending. M0 (which addresses the LDS side) is saved and restored inside
+// the block, so the compiler's view of it never changes; the s_nop is the wait state between a
+// write of M0 and its use by the load.
 struct BufDesc {
   uint32_t w[4];
 };
@@ -56,13 +57,36 @@ __device__ inline BufDesc make_desc(const void* base, uint32_t bytes) {
 __device__ inline void dma16(const BufDesc& d, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 rs = u32x4{d.w[0], d.w[1], d.w[2], d.w[3]};
+  uint32_t saved;
   asm volatile(
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %0, %1, %3 offen lds"
-      :
+      "buffer_load_dwordx4 %1, %2, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
       : "v"(voff), "s"(rs), "s"(lds_addr), "s"(soff)
-      : "memory", "m0");
+      : "memory");
+}
+// LDS reads addressed by 32-bit LDS byte addresses. Going through an integer address (instead of a
+// generic pointer) lets the compiler put constant displacements into the instruction's offset field
+// instead of recomputing each address with vector adds.
+typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+__device__ inline i32x4 lds_read_b128(uint32_t addr) { return *(const lds_i32x4*)(uintptr_t)addr; }
+__device__ inline i32x2 lds_read_tr16(uint32_t addr) {
+  return __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)addr));
+}
+__device__ inline i32x2 lds_read_tr8(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(uintptr_t)addr);
+}
+// Hides a per-lane LDS base address from the optimiser. Without it, the compiler reassociates
+// base + lane_offset + constant into base + (lane_offset + constant) with one register per
+// constant, and every read pays a vector add; with an opaque base the constant stays in the
+// instruction's offset field.
+__device__ inline uint32_t opaque_vbase(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 __device__ inline uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;

@@ -29,7 +29,6 @@
 namespace fa {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 // log2 of the 2^8 shift applied to p before its e4m3 rounding, and the reference threshold.
 constexpr float kPShiftLog2 = 8.0f;
@@ -171,14 +170,19 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_fp8_kernel(FwdArgs a) {
   }
 
   auto compute_s = [&](const char* ks, f32x16* s) {
+    uint32_t kbase[KS][2];
+#pragma unroll
+    for (int k = 0; k < KS; ++k)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) kbase[k][c] = opaque_vbase(lds_addr_of(ks) + koff[k][c]);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const i32x4 x0 = *(const i32x4*)(ks + kb * 32 * ROWB + koff[k][0]);
-        const i32x4 x1 = *(const i32x4*)(ks + kb * 32 * ROWB + koff[k][1]);
+        const i32x4 x0 = lds_read_b128(kbase[k][0] + kb * 32 * ROWB);
+        const i32x4 x1 = lds_read_b128(kbase[k][1] + kb * 32 * ROWB);
         s[kb] = mfma_fp8(i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]}, qop[k], s[kb]);
       }
     }
@@ -217,13 +221,13 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_fp8_kernel(FwdArgs a) {
       i32x8 vop[DB];
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
+        const uint32_t vbase = opaque_vbase(lds_addr_of(vs) + voff[db]);
         i32x2 part[4];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int pr = 0; pr < 2; ++pr)
-            part[kb * 2 + pr] =
-                __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vs + (kb * 32 + pr * 8) * ROWB + voff[db]));
+            part[kb * 2 + pr] = lds_read_tr8(vbase + (kb * 32 + pr * 8) * ROWB);
         vop[db] = i32x8{part[0][0], part[0][1], part[1][0], part[1][1], part[2][0], part[2][1], part[3][0], part[3][1]};
       }
       if (tile_partial(t)) {

@@ -180,9 +180,17 @@ def test_causal_4096_tile_counts():
 
 
 def test_plan(lib):
+    # 4 waves of 32 query rows per workgroup: 32 query tiles of 128 rows, and query tile qt visits
+    # 2 (qt + 1) key tiles of 64 under a causal mask
     p = fa.plan(4, 4096, 4096, 32, 32, 64, causal=True)
-    assert p["block_m"] == 128 and p["block_n"] == 64 and p["num_q_tiles"] == 32
+    assert p["block_m"] == 128 and p["block_n"] == 64 and p["waves"] == 4 and p["num_q_tiles"] == 32
     assert p["grid"] == 4 * 32 * 32
     assert p["kv_tiles"] == 4 * 32 * sum(2 * (t + 1) for t in range(32))
+    # D = 128 runs the 4-wave kernel (128 rows per workgroup)
+    p = fa.plan(1, 16384, 16384, 32, 8, 128, causal=True, dtype=fa.FA_BF16)
+    assert p["block_m"] == 128 and p["waves"] == 4 and p["num_q_tiles"] == 128
+    # fp8: 4-wave kernel
+    p = fa.plan(2, 4096, 4096, 32, 32, 64, causal=True, dtype=fa.FA_FP8_E4M3)
+    assert p["block_m"] == 128 and p["grid"] == 2 * 32 * 32
     with pytest.raises(fa.FaError):
         fa.plan(1, 128, 128, 3, 2, 64)
