@@ -46,7 +46,9 @@ __device__ inline float pair_sum(float x) {
 // these loads itself (vmcnt before each barrier). There is no destination register: nothing in the
 // register file is left pending. M0 (which addresses the LDS side) is saved and restored inside
 // the block, so the compiler's view of it never changes; the s_nop is the wait state between a
-// write of M0 and its use by the load.
+// write of M0 and its use by the load. The LDS address and the offset are wave-uniform; they pass
+// through readfirstlane because the compiler sometimes keeps a uniform loop value in a vector
+// register, and the instruction takes scalar operands only.
 struct BufDesc {
   uint32_t w[4];
 };
@@ -65,7 +67,7 @@ __device__ inline void dma16(const BufDesc& d, uint32_t voff, uint32_t soff, uin
       "buffer_load_dwordx4 %1, %2, %4 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(voff), "s"(rs), "s"(lds_addr), "s"(soff)
+      : "v"(voff), "s"(rs), "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "s"(__builtin_amdgcn_readfirstlane(soff))
       : "memory");
 }
 // LDS reads addressed by 32-bit LDS byte addresses. Going through an integer address (instead of a

@@ -96,16 +96,21 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   const int w0 = q0 + wave * 32;
   const bool wave_live = w0 < a.Nq;
   const int w1 = min(w0 + 31, a.Nq - 1);
-  // Key bounds of the wave's first and last rows, clamped to [-1, Nk] (wave-uniform scalars):
-  // a tile is skipped if it ends before lo(w0) or starts after hi(w1), and needs no mask if it
-  // lies inside [lo(w1), hi(w0)].
+  // Key bounds of the wave's first and last rows, clamped to [-1, Nk] (wave-uniform scalars).
+  // Each row admits an interval of keys and both ends grow with the row, so the tiles holding
+  // an admitted key for some row of the wave form an interval [jlo, jhi), and the tiles admitted
+  // for every row another one, [flo, fhi), inside it.
   auto clamp_key = [&](int64_t x) { return (int)(x < -1 ? -1 : (x > a.Nk ? a.Nk : x)); };
   const int wlo0 = __builtin_amdgcn_readfirstlane(clamp_key(key_lo(ms, w0)));
   const int wlo1 = __builtin_amdgcn_readfirstlane(clamp_key(key_lo(ms, w1)));
   const int whi0 = __builtin_amdgcn_readfirstlane(clamp_key(key_hi(ms, w0)));
   const int whi1 = __builtin_amdgcn_readfirstlane(clamp_key(key_hi(ms, w1)));
-  auto tile_live = [&](int t) { return wave_live && t * BN + BN - 1 >= wlo0 && t * BN <= whi1; };
-  auto tile_partial = [&](int t) { return !(wlo1 <= t * BN && t * BN + BN - 1 <= whi0); };
+  int jlo = 0, jhi = 0;
+  if (wave_live && whi1 >= wlo0) {
+    jlo = max(tb, wlo0 / BN);
+    jhi = min(te, whi1 / BN + 1);
+  }
+  const int flo = (wlo1 + BN - 1) / BN, fhi = (whi0 + 1) / BN;
   const int my_row = w0 + l32;
   const int lo_i = clamp_key(key_lo(ms, my_row));
   const int hi_i = clamp_key(key_hi(ms, my_row));
@@ -131,11 +136,11 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
     vgoff[i] = (uint32_t)row * v_rowb + ((pc ^ v_swz<ROWB>(row)) << 4);
   }
   const BufDesc k_d = make_desc(kbp, a.k_bytes), v_d = make_desc(vbp, a.v_bytes);
-  auto dma = [&](const BufDesc& d, const uint32_t* goff, uint32_t rowb, int t, char* slot) {
-    const uint32_t base = (uint32_t)(t * BN) * rowb;
-    const uint32_t lds = lds_addr_of(slot) + wave * 64 * 16;
+  const uint32_t kring_a = lds_addr_of(kring), vring_a = lds_addr_of(vring);
+  // The CH loads of one tile: soff is the tile's byte offset in the head, lds its ring slot.
+  auto dma = [&](const BufDesc& d, const uint32_t* goff, uint32_t soff, uint32_t lds) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) dma16(d, goff[i], base, lds + i * NT * 16);
+    for (int i = 0; i < CH; ++i) dma16(d, goff[i], soff, lds + wave * 64 * 16 + i * NT * 16);
   };
   // Barrier that waits only for this thread's loads older than the newest `pending` ones: a
   // compiler-only fence keeps LDS accesses on their side, and no blanket vmcnt(0) is emitted.
@@ -162,134 +167,200 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
     voff[db] = (4 * (g16 >> 1) + tr) * ROWB + ((chunk ^ v_swz<ROWB>(tr)) << 4) + (tc & 1) * 8;
   }
 
-  auto compute_s = [&](const char* ks, f32x16* s) {
-    uint32_t kbase[KS];
-#pragma unroll
-    for (int k = 0; k < KS; ++k) kbase[k] = opaque_vbase(lds_addr_of(ks) + koff[k]);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      i32x4 kop[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) kop[kb] = lds_read_b128(kbase[k] + kb * 32 * ROWB);
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) s[kb] = TR::mfma(kop[kb], qop[k], s[kb]);
-    }
-  };
-
   const float c2 = a.scale_log2;
-  float m = -INFINITY;   // reference max of score * c2 for this lane's query
+  // Reference max of score * c2 for this lane's query. It starts at a huge negative finite value
+  // rather than -inf: the first tile with an admitted key then overflows the sum bound and sets
+  // the reference (see kSumBound), while a fully masked tile still gives p = exp2(-inf) = 0.
+  float m = -1e30f;
   float l = 0.f;         // this lane's share of the running sum (lanes l, l^32 split the keys)
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
 
-  // ---- pipeline fill: K(tb), V(tb), K(tb+1) landed; S(tb); V(tb+1), K(tb+2) in flight
-  if (tb < te) {
-    dma(k_d, kgoff, k_rowb, tb, kring);
-    dma(v_d, vgoff, v_rowb, tb, vring);
-    if (tb + 1 < te) dma(k_d, kgoff, k_rowb, tb + 1, kring + TILEB);
-  }
-  barrier_keep(0);
-  f32x16 sa[KB], sb[KB];
-  if (tb < te && tile_live(tb)) compute_s(kring, sa);
-  if (tb + 1 < te) dma(v_d, vgoff, v_rowb, tb + 1, vring + TILEB);
-  if (tb + 2 < te) dma(k_d, kgoff, k_rowb, tb + 2, kring + 2 * TILEB);
-  barrier_keep(2 * CH);    // K(tb) fully read by every wave before its slot is reused
-
-  // One pipeline step: S(t+1) into sn while tile t (scores in sc) goes through the softmax and
-  // the PV product. Two steps per loop trip swap the roles of the two S arrays.
-  auto step = [&](int t, f32x16 (&sc)[KB], f32x16 (&sn)[KB]) {
-    const int i = t - tb;
-    const int s0 = i % NS, s1 = (i + 1) % NS, s2 = (i + 2) % NS;   // ring slots of tiles t, t+1, t+2
-    const bool k3 = t + 3 < te, v2 = t + 2 < te;
-    // K(t+3) into K(t)'s slot (read last step); V(t+2) into V(t-1)'s slot (read last step)
-    if (k3) dma(k_d, kgoff, k_rowb, t + 3, kring + s0 * TILEB);
-    if (v2) dma(v_d, vgoff, v_rowb, t + 2, vring + s2 * TILEB);
-    if (t + 1 < te && tile_live(t + 1)) compute_s(kring + s1 * TILEB, sn);
-    if (tile_live(t)) {
-      const int j0 = t * BN;
-      // V^T operands for this tile
-      i32x4 vop[KB][2][DB];
-      {
-        const char* vs = vring + s0 * TILEB;
-        uint32_t vbase[DB];
+  // ---- building blocks of one step. Operands are read from LDS through opaque per-slot bases so
+  // the per-read displacements stay in the instruction's offset field.
+  auto read_k = [&](uint32_t slot, i32x4 (&kop)[KS][KB]) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) vbase[db] = opaque_vbase(lds_addr_of(vs) + voff[db]);
+    for (int k = 0; k < KS; ++k) {
+      const uint32_t base = opaque_vbase(slot + koff[k]);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb) kop[k][kb] = lds_read_b128(base + kb * 32 * ROWB);
+    }
+  };
+  auto read_v = [&](uint32_t slot, i32x4 (&vop)[KB][2][DB]) {
 #pragma unroll
-          for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-              const uint32_t p = vbase[db] + (kb * 32 + half * 16) * ROWB;
-              const i32x2 v0 = lds_read_tr16(p), v1r = lds_read_tr16(p + 8 * ROWB);
-              vop[kb][half][db] = i32x4{v0[0], v0[1], v1r[0], v1r[1]};
-            }
-      }
-      // mask (partial tiles only): key of accumulator r in block kb is j0 + kb*32 + (r/4)*8 + hl*4 + r%4
-      if (tile_partial(t)) {
-        const int jl = j0 + hl * 4 - lo_i;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = jl + kb * 32 + (r >> 2) * 8 + (r & 3);
-            sc[kb][r] = (uint32_t)j < span_i ? sc[kb][r] : -INFINITY;
-          }
-      }
-      // p = exp2(s * c - m), packed to the MFMA type, and the row sum
-      uint32_t pk[KB][8];
-      float rs;
-      auto exponentiate = [&](float mref) {
-        rs = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], c2, -mref));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r + 1], c2, -mref));
-            pk[kb][r >> 1] = TR::pack(p0, p1);
-            rs = TR::sum2(rs, pk[kb][r >> 1], p0, p1);
-          }
-      };
-      exponentiate(m);
-      if (__builtin_amdgcn_ballot_w64(!(rs <= kSumBound))) {
-        // slow path: move the reference to the running max, rescale, recompute
-        float mx = sc[0][0];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-        const float m_new = fmaxf(m, pair_max(mx) * c2);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] *= alpha;
-        m = m_new;
-        exponentiate(m_use);
-      }
-      l += rs;
-      // O^T += V^T P^T
+    for (int db = 0; db < DB; ++db) {
+      const uint32_t base = opaque_vbase(slot + voff[db]);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const i32x4 pop = i32x4{(int)pk[kb][4 * half + 0], (int)pk[kb][4 * half + 1], (int)pk[kb][4 * half + 2],
-                                  (int)pk[kb][4 * half + 3]};
-#pragma unroll
-          for (int db = 0; db < DB; ++db) o[db] = TR::mfma(vop[kb][half][db], pop, o[db]);
+          const uint32_t p = base + (kb * 32 + half * 16) * ROWB;
+          const i32x2 v0 = lds_read_tr16(p), v1 = lds_read_tr16(p + 8 * ROWB);
+          vop[kb][half][db] = i32x4{v0[0], v0[1], v1[0], v1[1]};
         }
     }
-    // K(t+2) and V(t+1) must have landed for the next step; this step's loads stay in flight
-    barrier_keep(CH * ((int)k3 + (int)v2));
+  };
+  // S MFMA number e of a tile (k-step e / KB, key block e % KB): consecutive MFMAs alternate
+  // accumulators, so dependent ones are KB apart.
+  auto mfma_s = [&](const i32x4 (&kop)[KS][KB], f32x16 (&s)[KB], int e) {
+    const int k = e / KB, kb = e % KB;
+    s[kb] = TR::mfma(kop[k][kb], qop[k], s[kb]);
+  };
+  // PV MFMA number e of a tile (key block e / (2 DB), half (e / DB) % 2, column block e % DB).
+  auto mfma_pv = [&](const i32x4 (&vop)[KB][2][DB], const uint32_t (&pk)[KB][8], int e) {
+    const int kb = e / (2 * DB), half = (e / DB) % 2, db = e % DB;
+    const i32x4 pop = i32x4{(int)pk[kb][4 * half + 0], (int)pk[kb][4 * half + 1], (int)pk[kb][4 * half + 2],
+                            (int)pk[kb][4 * half + 3]};
+    o[db] = TR::mfma(vop[kb][half][db], pop, o[db]);
+  };
+  // Softmax of score pair number i (key block i / 8, accumulator entries 2 (i % 8) and + 1):
+  // p = exp2(s * c - mref), packed to the MFMA type, added to the row sum.
+  auto p_pair = [&](const f32x16 (&sc)[KB], uint32_t (&pk)[KB][8], float& rs, float mref, int i) {
+    const int kb = i / 8, r = (i % 8) * 2;
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], c2, -mref));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r + 1], c2, -mref));
+    pk[kb][r >> 1] = TR::pack(p0, p1);
+    rs = TR::sum2(rs, pk[kb][r >> 1], p0, p1);
+  };
+  constexpr int NSM = KS * KB;          // S MFMAs per tile
+  constexpr int NPV = KB * 2 * DB;      // PV MFMAs per tile
+  constexpr int NPAIR = KB * 8;         // score pairs per lane per tile
+  static_assert(NSM == NPV && (2 * NSM) % NPAIR == 0, "the interleave pairs S and PV MFMAs one to one");
+  auto softmax_all = [&](f32x16 (&sc)[KB], uint32_t (&pk)[KB][8], float& rs, float mref) {
+    rs = 0.f;
+#pragma unroll
+    for (int i = 0; i < NPAIR; ++i) p_pair(sc, pk, rs, mref, i);
+  };
+  // Rebase when a p may exceed the bound (see kSumBound): m moves to the running max, O and l
+  // are rescaled, p is recomputed. O must already hold every PV product issued against the old m.
+  auto check_rebase = [&](f32x16 (&sc)[KB], uint32_t (&pk)[KB][8], float& rs) {
+    if (__builtin_amdgcn_ballot_w64(!(rs <= kSumBound))) {
+      float mx = sc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+      const float m_new = fmaxf(m, pair_max(mx) * c2);   // finite: m starts finite
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      m = m_new;
+      softmax_all(sc, pk, rs, m);
+    }
+    l += rs;
+  };
+  auto mask_tile = [&](f32x16 (&sc)[KB], int t) {
+    // key of accumulator r in block kb is t*BN + kb*32 + (r/4)*8 + hl*4 + r%4
+    const int jl = t * BN + hl * 4 - lo_i;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = jl + kb * 32 + (r >> 2) * 8 + (r & 3);
+        sc[kb][r] = (uint32_t)j < span_i ? sc[kb][r] : -INFINITY;
+      }
   };
 
-  for (int t = tb; t < te; t += 2) {
-    step(t, sa, sb);
-    if (t + 1 < te) step(t + 1, sb, sa);
+  // ---- software pipeline. Step j: loads of K(j+3) and V(j+1) are issued; then PV(j-1) and
+  // S(j+1) run on the matrix pipe while the softmax of tile j (scores computed in step j-1) runs
+  // on the vector pipe. PV lags one tile so that its operand P(j-1) is ready at the start of the
+  // step. The three products of a step are independent and are issued as one interleaved
+  // sequence: each MFMA is followed by the softmax of a share of the tile's scores, so a single
+  // wave keeps both pipes busy.
+  // A wave runs this sequence in every step from jlo - 1 to jhi (the tiles it needs, plus one on
+  // each side for the lagging PV and the leading S) and skips the others; tiles outside its
+  // interval are masked like partial ones, so their P is exactly zero and their PV adds nothing.
+  // Tile j of either tensor sits in ring slot (j - tb) % 3; a slot is refilled one step after
+  // its last read, behind the step's closing barrier. r0, r1, r2 are the byte offsets of slots
+  // (j - tb) % 3, (j - tb + 1) % 3 and (j - tb + 2) % 3.
+  const int need_lo = jlo - 1;
+  const uint32_t need_n = jlo < jhi ? (uint32_t)(jhi - jlo + 2) : 0u;
+  const uint32_t full_n = fhi > flo ? (uint32_t)(fhi - flo) : 0u;
+  uint32_t r0 = 0, r1 = TILEB, r2 = 2 * TILEB;
+  uint32_t k_soff = (uint32_t)((tb + 3) * BN) * k_rowb;   // byte offset of K(j+3)
+  uint32_t v_soff = (uint32_t)((tb + 1) * BN) * v_rowb;   // byte offset of V(j+1)
+
+  // V slot 2 stands for V(tb-1), read (against P = 0) by the first step before any load fills
+  // it: zero it so that the product is exactly zero.
+#pragma unroll
+  for (int c = tid * 16; c < TILEB; c += NT * 16) *(i32x4*)(vring + 2 * TILEB + c) = i32x4{};
+  // prologue: K(tb), K(tb+1), V(tb), K(tb+2) in flight; K(tb) and K(tb+1) landed; S(tb)
+  if (tb < te) {
+    dma(k_d, kgoff, (uint32_t)(tb * BN) * k_rowb, kring_a);
+    if (tb + 1 < te) dma(k_d, kgoff, (uint32_t)((tb + 1) * BN) * k_rowb, kring_a + TILEB);
+    dma(v_d, vgoff, (uint32_t)(tb * BN) * v_rowb, vring_a);
+    if (tb + 2 < te) dma(k_d, kgoff, (uint32_t)((tb + 2) * BN) * k_rowb, kring_a + 2 * TILEB);
+  }
+  // V(tb) and K(tb+2) may stay in flight
+  const int pro_pending = tb < te ? CH * (1 + (int)(tb + 2 < te)) : 0;
+  barrier_keep(pro_pending);
+  f32x16 sa[KB], sb[KB];
+  uint32_t pa[KB][8], pb[KB][8];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) pa[kb][r] = pb[kb][r] = 0u;
+  {
+    i32x4 kop[KS][KB];
+    read_k(kring_a, kop);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sa[kb] = f32x16{};
+#pragma unroll
+    for (int e = 0; e < NSM; ++e) mfma_s(kop, sa, e);
+  }
+  barrier_keep(pro_pending);   // every wave has read K(tb) before step tb refills its slot
+
+  auto step = [&](int j, f32x16 (&sc)[KB], f32x16 (&sn)[KB], const uint32_t (&pp)[KB][8], uint32_t (&pc)[KB][8]) {
+    const bool k3 = j + 3 < te, v1 = j + 1 < te;
+    if (k3) dma(k_d, kgoff, k_soff, kring_a + r0);
+    if (v1) dma(v_d, vgoff, v_soff, vring_a + r1);
+    if ((uint32_t)(j - need_lo) < need_n) {
+      if (!((uint32_t)(j - flo) < full_n)) mask_tile(sc, j);
+      i32x4 kop[KS][KB];
+      i32x4 vop[KB][2][DB];
+      read_k(kring_a + r1, kop);      // K(j+1)
+      read_v(vring_a + r2, vop);      // V(j-1)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) sn[kb] = f32x16{};
+      float rs = 0.f;
+      // All operands are in registers before the first MFMA. Measured on MI355X, one wait here
+      // beats waits spread through the sequence.
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      __builtin_amdgcn_sched_barrier(0);
+      constexpr int PER = 2 * NSM / NPAIR;   // MFMAs per score pair
+#pragma unroll
+      for (int e = 0; e < 2 * NSM; ++e) {
+        if (e % 2 == 0) mfma_s(kop, sn, e / 2);
+        else mfma_pv(vop, pp, e / 2);
+        if (e % PER == PER - 1) {
+          const int pi = e / PER;
+          p_pair(sc, pc, rs, m, pi);
+          // keep the pair in this group (the compiler would otherwise gather the softmax)
+          asm volatile("" ::"v"(pc[pi / 8][pi % 8]), "v"(rs));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      check_rebase(sc, pc, rs);
+    }
+    // K(j+2) and V(j) must have landed for the next step; this step's loads stay in flight
+    barrier_keep(CH * ((int)k3 + (int)v1));
+    const uint32_t rt = r0;
+    r0 = r1;
+    r1 = r2;
+    r2 = rt;
+    k_soff = __builtin_amdgcn_readfirstlane(k_soff + BN * k_rowb);
+    v_soff = __builtin_amdgcn_readfirstlane(v_soff + BN * v_rowb);
+  };
+
+  // Steps tb .. te; the last one only drains PV(te-1). Two steps per trip swap the roles of the
+  // S and P arrays; the exits after either step keep the loop-carried values in place.
+  for (int t = tb;; t += 2) {
+    step(t, sa, sb, pb, pa);
+    if (t + 1 > te) break;
+    step(t + 1, sb, sa, pa, pb);
+    if (t + 2 > te) break;
   }
 
   // ---- epilogue: O / l, lse = (m + log2 l) * ln 2
