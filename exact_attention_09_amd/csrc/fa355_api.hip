@@ -18,7 +18,9 @@ hipError_t launch_fwd_fp8(const FwdArgs& a, int D, int64_t grid, hipStream_t str
 
 TileShape tile_shape(int D, int dtype) {
   TileShape t;
-  t.waves = 4;
+  // fp16/bf16 at D = 128: 8 waves (two per SIMD, the register budget allows no more); otherwise
+  // 4 waves, two workgroups per compute unit
+  t.waves = (dtype != FA_FP8_E4M3 && D == 128) ? 8 : 4;
   t.block_m = 32 * t.waves;
   t.block_n = 64;
   const int es = dtype == FA_FP8_E4M3 ? 1 : 2;

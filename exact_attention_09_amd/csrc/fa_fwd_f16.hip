@@ -177,42 +177,16 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
 
-  // ---- building blocks of one step. Operands are read from LDS through opaque per-slot bases so
-  // the per-read displacements stay in the instruction's offset field.
-  auto read_k = [&](uint32_t slot, i32x4 (&kop)[KS][KB]) {
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      const uint32_t base = opaque_vbase(slot + koff[k]);
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) kop[k][kb] = lds_read_b128(base + kb * 32 * ROWB);
-    }
-  };
-  auto read_v = [&](uint32_t slot, i32x4 (&vop)[KB][2][DB]) {
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const uint32_t base = opaque_vbase(slot + voff[db]);
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const uint32_t p = base + (kb * 32 + half * 16) * ROWB;
-          const i32x2 v0 = lds_read_tr16(p), v1 = lds_read_tr16(p + 8 * ROWB);
-          vop[kb][half][db] = i32x4{v0[0], v0[1], v1[0], v1[1]};
-        }
-    }
-  };
+  // ---- building blocks of one step
   // S MFMA number e of a tile (k-step e / KB, key block e % KB): consecutive MFMAs alternate
   // accumulators, so dependent ones are KB apart.
-  auto mfma_s = [&](const i32x4 (&kop)[KS][KB], f32x16 (&s)[KB], int e) {
-    const int k = e / KB, kb = e % KB;
-    s[kb] = TR::mfma(kop[k][kb], qop[k], s[kb]);
-  };
+  auto mfma_s = [&](const i32x4& kop, f32x16 (&s)[KB], int e) { s[e % KB] = TR::mfma(kop, qop[e / KB], s[e % KB]); };
   // PV MFMA number e of a tile (key block e / (2 DB), half (e / DB) % 2, column block e % DB).
-  auto mfma_pv = [&](const i32x4 (&vop)[KB][2][DB], const uint32_t (&pk)[KB][8], int e) {
+  auto mfma_pv = [&](const i32x4& vop, const uint32_t (&pk)[KB][8], int e) {
     const int kb = e / (2 * DB), half = (e / DB) % 2, db = e % DB;
     const i32x4 pop = i32x4{(int)pk[kb][4 * half + 0], (int)pk[kb][4 * half + 1], (int)pk[kb][4 * half + 2],
                             (int)pk[kb][4 * half + 3]};
-    o[db] = TR::mfma(vop[kb][half][db], pop, o[db]);
+    o[db] = TR::mfma(vop, pop, o[db]);
   };
   // Softmax of score pair number i (key block i / 8, accumulator entries 2 (i % 8) and + 1):
   // p = exp2(s * c - mref), packed to the MFMA type, added to the row sum.
@@ -303,12 +277,14 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) pa[kb][r] = pb[kb][r] = 0u;
   {
-    i32x4 kop[KS][KB];
-    read_k(kring_a, kop);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) sa[kb] = f32x16{};
 #pragma unroll
-    for (int e = 0; e < NSM; ++e) mfma_s(kop, sa, e);
+    for (int k = 0; k < KS; ++k) {
+      const uint32_t base = opaque_vbase(kring_a + koff[k]);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) mfma_s(lds_read_b128(base + kb * 32 * ROWB), sa, k * KB + kb);
+    }
   }
   barrier_keep(pro_pending);   // every wave has read K(tb) before step tb refills its slot
 
@@ -318,22 +294,45 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
     if (v1) dma(v_d, vgoff, v_soff, vring_a + r1);
     if ((uint32_t)(j - need_lo) < need_n) {
       if (!((uint32_t)(j - flo) < full_n)) mask_tile(sc, j);
-      i32x4 kop[KS][KB];
-      i32x4 vop[KB][2][DB];
-      read_k(kring_a + r1, kop);      // K(j+1)
-      read_v(vring_a + r2, vop);      // V(j-1)
+      // Operand of MFMA e of the sequence (even e: S, K from LDS; odd e: PV, V^T from LDS), read
+      // PF MFMAs ahead of its use. At D = 64 every read is issued up front (registers allow it
+      // and it measured fastest); at D = 128 a short distance keeps the kernel within 256
+      // registers, so two waves share each SIMD.
+      const uint32_t kslot = kring_a + r1, vslot = vring_a + r2;   // K(j+1), V(j-1)
+      uint32_t kbase[KS], vbase[DB];
+#pragma unroll
+      for (int k = 0; k < KS; ++k) kbase[k] = opaque_vbase(kslot + koff[k]);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) vbase[db] = opaque_vbase(vslot + voff[db]);
+      constexpr int NM = 2 * NSM, PF = D == 64 ? NM : 3;
+      i32x4 opnd[NM];
+      auto read_operand = [&](int e) {
+        const int idx = e / 2;
+        if (e % 2 == 0) {
+          opnd[e] = lds_read_b128(kbase[idx / KB] + (idx % KB) * 32 * ROWB);
+        } else {
+          const int kb = idx / (2 * DB), half = (idx / DB) % 2, db = idx % DB;
+          const uint32_t p = vbase[db] + (kb * 32 + half * 16) * ROWB;
+          const i32x2 v0 = lds_read_tr16(p), v1 = lds_read_tr16(p + 8 * ROWB);
+          opnd[e] = i32x4{v0[0], v0[1], v1[0], v1[1]};
+        }
+      };
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) sn[kb] = f32x16{};
       float rs = 0.f;
-      // All operands are in registers before the first MFMA. Measured on MI355X, one wait here
-      // beats waits spread through the sequence.
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+#pragma unroll
+      for (int e = 0; e < PF; ++e) read_operand(e);
+      if constexpr (PF == NM) __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      // The sequence runs at raised issue priority: when both waves of a SIMD are ready, the one
+      // inside its sequence (which feeds both pipes) issues first.
+      __builtin_amdgcn_s_setprio(1);
       __builtin_amdgcn_sched_barrier(0);
       constexpr int PER = 2 * NSM / NPAIR;   // MFMAs per score pair
 #pragma unroll
-      for (int e = 0; e < 2 * NSM; ++e) {
-        if (e % 2 == 0) mfma_s(kop, sn, e / 2);
-        else mfma_pv(vop, pp, e / 2);
+      for (int e = 0; e < NM; ++e) {
+        if (e + PF < NM) read_operand(e + PF);
+        if (e % 2 == 0) mfma_s(opnd[e], sn, e / 2);
+        else mfma_pv(opnd[e], pp, e / 2);
         if (e % PER == PER - 1) {
           const int pi = e / PER;
           p_pair(sc, pc, rs, m, pi);
@@ -342,6 +341,7 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(0);
       check_rebase(sc, pc, rs);
     }
     // K(j+2) and V(j) must have landed for the next step; this step's loads stay in flight
@@ -384,7 +384,7 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
 
 template <class TR, int D>
 static hipError_t launch_t(const FwdArgs& a, int64_t grid, hipStream_t stream) {
-  constexpr int BN = 64, WAVES = 4;
+  constexpr int BN = 64, WAVES = D == 64 ? 4 : 8;
   hipLaunchKernelGGL((fa_fwd_kernel<TR, D, BN, WAVES>), dim3((unsigned)grid), dim3(WAVES * 64), 0, stream, a);
   return hipGetLastError();
 }

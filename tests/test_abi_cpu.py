@@ -186,9 +186,9 @@ def test_plan(lib):
     assert p["block_m"] == 128 and p["block_n"] == 64 and p["waves"] == 4 and p["num_q_tiles"] == 32
     assert p["grid"] == 4 * 32 * 32
     assert p["kv_tiles"] == 4 * 32 * sum(2 * (t + 1) for t in range(32))
-    # D = 128 runs the 4-wave kernel (128 rows per workgroup)
+    # D = 128 runs 8 waves (256 rows per workgroup)
     p = fa.plan(1, 16384, 16384, 32, 8, 128, causal=True, dtype=fa.FA_BF16)
-    assert p["block_m"] == 128 and p["waves"] == 4 and p["num_q_tiles"] == 128
+    assert p["block_m"] == 256 and p["waves"] == 8 and p["num_q_tiles"] == 64
     # fp8: 4-wave kernel
     p = fa.plan(2, 4096, 4096, 32, 32, 64, causal=True, dtype=fa.FA_FP8_E4M3)
     assert p["block_m"] == 128 and p["grid"] == 2 * 32 * 32
