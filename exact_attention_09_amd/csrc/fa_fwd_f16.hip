@@ -69,12 +69,28 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   const int l32 = lane & 31;     // query column of this lane inside the wave's 32 rows
 
   // ---- which (batch, head, query tile) this workgroup computes
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = L / a.num_q_tiles;
-  int qt = L - bh * a.num_q_tiles;
-  if (a.causal) qt = a.num_q_tiles - 1 - qt;     // heaviest tiles of a head first
-  const int b = bh / a.Hq;
-  const int h = bh - b * a.Hq;
+  int b, h, qt;
+  if (a.causal) {
+    // Causal query tiles differ in length by up to the number of tiles; all heads' tiles of one
+    // length run before any shorter ones (longest first, which keeps the tail of the launch
+    // short). Within a length, consecutive workgroups (dealt round-robin over the 8 XCDs) take
+    // consecutive K/V heads, so the query heads sharing a K/V head land on the same XCD.
+    const int n_bh = gridDim.x / a.num_q_tiles;
+    const int rank = blockIdx.x / n_bh;
+    const int idx = blockIdx.x - rank * n_bh;
+    const int hkv = a.Hq / a.group, n_kvh = n_bh / a.group;
+    const int g = idx / n_kvh, kvh = idx - g * n_kvh;
+    b = kvh / hkv;
+    h = (kvh - b * hkv) * a.group + g;
+    qt = a.num_q_tiles - 1 - rank;
+  } else {
+    // equal tiles: a head's tiles stay together on one XCD, whose L2 then holds its K/V
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = L / a.num_q_tiles;
+    qt = L - bh * a.num_q_tiles;
+    b = bh / a.Hq;
+    h = bh - b * a.Hq;
+  }
   const int hk = h / a.group;                    // MQA/GQA: K/V head of this query head
   const int q0 = qt * BM;
 
@@ -116,14 +132,9 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   const int hi_i = clamp_key(key_hi(ms, my_row));
   const uint32_t span_i = hi_i >= lo_i ? (uint32_t)(hi_i - lo_i + 1) : 0u;
 
-  // ---- Q operands (B operand of S^T): row my_row, head-dim slots ks*16 + hl*8 .. +7
+  // Q operands (B operand of S^T): row my_row, head-dim slots ks*16 + hl*8 .. +7; loaded in the
+  // prologue, behind the first K/V tile loads
   i32x4 qop[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    qop[ks] = __builtin_amdgcn_raw_buffer_load_b128(q_r, (uint32_t)my_row * q_rowb + (ks * 16 + hl * 8) * ES, 0, 0);
-  // Q must have landed before the pipelined loop: without this wait the compiler's wait-count
-  // analysis, merging the loop back edge, would make every iteration wait on the prefetches.
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
   // ---- HBM -> LDS loads of one K or V tile. Load i of a thread writes the 16 bytes at slot
   // position P = (i * NT + tid) * 16; P holds row P / ROWB, physical chunk (P % ROWB) / 16, i.e.
@@ -267,9 +278,14 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
     dma(v_d, vgoff, (uint32_t)(tb * BN) * v_rowb, vring_a);
     if (tb + 2 < te) dma(k_d, kgoff, (uint32_t)((tb + 2) * BN) * k_rowb, kring_a + 2 * TILEB);
   }
-  // V(tb) and K(tb+2) may stay in flight
-  const int pro_pending = tb < te ? CH * (1 + (int)(tb + 2 < te)) : 0;
-  barrier_keep(pro_pending);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qop[ks] = __builtin_amdgcn_raw_buffer_load_b128(q_r, (uint32_t)my_row * q_rowb + (ks * 16 + hl * 8) * ES, 0, 0);
+  // Q (and with it the first tiles) must have landed before the pipelined loop: without this
+  // wait the compiler's wait-count analysis, merging the loop back edge, would make every
+  // iteration wait on the prefetches.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  barrier_keep(0);
   f32x16 sa[KB], sb[KB];
   uint32_t pa[KB][8], pb[KB][8];
 #pragma unroll
@@ -286,7 +302,7 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
       for (int kb = 0; kb < KB; ++kb) mfma_s(lds_read_b128(base + kb * 32 * ROWB), sa, k * KB + kb);
     }
   }
-  barrier_keep(pro_pending);   // every wave has read K(tb) before step tb refills its slot
+  barrier_keep(0);   // every wave has read K(tb) before step tb refills its slot
 
   auto step = [&](int j, f32x16 (&sc)[KB], f32x16 (&sn)[KB], const uint32_t (&pp)[KB][8], uint32_t (&pc)[KB][8]) {
     const bool k3 = j + 3 < te, v1 = j + 1 < te;

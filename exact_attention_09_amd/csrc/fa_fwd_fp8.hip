@@ -104,13 +104,18 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_fp8_kernel(FwdArgs a) {
   const int w0 = q0 + wave * 32;
   const bool wave_live = w0 < a.Nq;
   const int w1 = min(w0 + 31, a.Nq - 1);
+  // tiles with an admitted key for some row of the wave: [jlo, jhi); for every row: [flo, fhi)
   auto clamp_key = [&](int64_t x) { return (int)(x < -1 ? -1 : (x > a.Nk ? a.Nk : x)); };
   const int wlo0 = __builtin_amdgcn_readfirstlane(clamp_key(key_lo(ms, w0)));
   const int wlo1 = __builtin_amdgcn_readfirstlane(clamp_key(key_lo(ms, w1)));
   const int whi0 = __builtin_amdgcn_readfirstlane(clamp_key(key_hi(ms, w0)));
   const int whi1 = __builtin_amdgcn_readfirstlane(clamp_key(key_hi(ms, w1)));
-  auto tile_live = [&](int t) { return wave_live && t * BN + BN - 1 >= wlo0 && t * BN <= whi1; };
-  auto tile_partial = [&](int t) { return !(wlo1 <= t * BN && t * BN + BN - 1 <= whi0); };
+  int jlo = 0, jhi = 0;
+  if (wave_live && whi1 >= wlo0) {
+    jlo = max(tb, wlo0 / BN);
+    jhi = min(te, whi1 / BN + 1);
+  }
+  const int flo = (wlo1 + BN - 1) / BN, fhi = (whi0 + 1) / BN;
   const int my_row = w0 + l32;
   const int lo_i = clamp_key(key_lo(ms, my_row));
   const int hi_i = clamp_key(key_hi(ms, my_row));
@@ -137,11 +142,10 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_fp8_kernel(FwdArgs a) {
     vgoff[i] = (uint32_t)v_key_of_row(row) * v_rowb + ((pc ^ v_swz8<ROWB>(row)) << 4);
   }
   const BufDesc k_d = make_desc(kbp, a.k_bytes), v_d = make_desc(vbp, a.v_bytes);
-  auto dma = [&](const BufDesc& d, const uint32_t* goff, uint32_t rowb, int t, char* slot) {
-    const uint32_t base = (uint32_t)(t * BN) * rowb;
-    const uint32_t lds = lds_addr_of(slot) + wave * 64 * 16;
+  const uint32_t kring_a = lds_addr_of(kring), vring_a = lds_addr_of(vring);
+  auto dma = [&](const BufDesc& d, const uint32_t* goff, uint32_t soff, uint32_t lds) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) dma16(d, goff[i], base, lds + i * NT * 16);
+    for (int i = 0; i < CH; ++i) dma16(d, goff[i], soff, lds + wave * 64 * 16 + i * NT * 16);
   };
   auto barrier_keep = [&](int pending) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -169,121 +173,161 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_fp8_kernel(FwdArgs a) {
     voff[db] = ((g16 >> 1) * 16 + tr8) * ROWB + ((chunk ^ v_swz8<ROWB>(tr8)) << 4) + tc8 * 8;
   }
 
-  auto compute_s = [&](const char* ks, f32x16* s) {
-    uint32_t kbase[KS][2];
-#pragma unroll
-    for (int k = 0; k < KS; ++k)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) kbase[k][c] = opaque_vbase(lds_addr_of(ks) + koff[k][c]);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const i32x4 x0 = lds_read_b128(kbase[k][0] + kb * 32 * ROWB);
-        const i32x4 x1 = lds_read_b128(kbase[k][1] + kb * 32 * ROWB);
-        s[kb] = mfma_fp8(i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]}, qop[k], s[kb]);
-      }
-    }
-  };
-
   const float c2 = a.scale_log2;
-  float m = -INFINITY;
+  // Reference of score * c2, starting at a huge negative finite value (a fully masked tile then
+  // gives p = 0 with no special case; the first admitted key moves it).
+  float m = -1e30f;
   float l = 0.f;         // sum of 2^8 * p over this lane's keys
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
 
-  if (tb < te) {
-    dma(k_d, kgoff, k_rowb, tb, kring);
-    dma(v_d, vgoff, v_rowb, tb, vring);
-    if (tb + 1 < te) dma(k_d, kgoff, k_rowb, tb + 1, kring + TILEB);
-  }
-  barrier_keep(0);
-  f32x16 sa[KB], sb[KB];
-  if (tb < te && tile_live(tb)) compute_s(kring, sa);
-  if (tb + 1 < te) dma(v_d, vgoff, v_rowb, tb + 1, vring + TILEB);
-  if (tb + 2 < te) dma(k_d, kgoff, k_rowb, tb + 2, kring + 2 * TILEB);
-  barrier_keep(2 * CH);
+  // S MFMA e (k-step e / KB, key block e % KB) and its K operand (two 16-byte LDS reads)
+  auto k_operand = [&](uint32_t slot, int e) {
+    const int k = e / KB, kb = e % KB;
+    const i32x4 x0 = lds_read_b128(opaque_vbase(slot + koff[k][0]) + kb * 32 * ROWB);
+    const i32x4 x1 = lds_read_b128(opaque_vbase(slot + koff[k][1]) + kb * 32 * ROWB);
+    return i32x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+  };
+  // V^T operand of column block db: 8 LDS rows per transpose read, 4 reads = the tile's 64 keys
+  auto v_operand = [&](uint32_t slot, int db) {
+    const uint32_t vbase = opaque_vbase(slot + voff[db]);
+    i32x2 part[4];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) part[kb * 2 + pr] = lds_read_tr8(vbase + (kb * 32 + pr * 8) * ROWB);
+    return i32x8{part[0][0], part[0][1], part[1][0], part[1][1], part[2][0], part[2][1], part[3][0], part[3][1]};
+  };
+  constexpr int NSM = KS * KB;          // S MFMAs per tile
+  auto mask_tile = [&](f32x16 (&sc)[KB], int t) {
+    const int jl = t * BN + hl * 4 - lo_i;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = jl + kb * 32 + (r >> 2) * 8 + (r & 3);
+        sc[kb][r] = (uint32_t)j < span_i ? sc[kb][r] : -INFINITY;
+      }
+  };
 
-  auto step = [&](int t, f32x16 (&sc)[KB], f32x16 (&sn)[KB]) {
-    const int i = t - tb;
-    const int s0 = i % NS, s1 = (i + 1) % NS, s2 = (i + 2) % NS;
-    const bool k3 = t + 3 < te, v2 = t + 2 < te;
-    if (k3) dma(k_d, kgoff, k_rowb, t + 3, kring + s0 * TILEB);
-    if (v2) dma(v_d, vgoff, v_rowb, t + 2, vring + s2 * TILEB);
-    if (t + 1 < te && tile_live(t + 1)) compute_s(kring + s1 * TILEB, sn);
-    if (tile_live(t)) {
-      const char* vs = vring + s0 * TILEB;
-      const int j0 = t * BN;
-      // V^T operands: for each column block, 8 LDS rows per read, 4 reads = 32 keys per lane
-      i32x8 vop[DB];
+  // ---- software pipeline, as in the 16-bit kernel: step j issues the loads of K(j+3) and V(j+1),
+  // runs PV(j-1) and S(j+1) on the matrix pipe and the softmax of tile j on the vector pipe.
+  // The softmax needs the tile's row max before its exponentials (the reference may have to
+  // move), so a step has two interleaved halves: PV(j-1) with the row max, then, after the
+  // reference update (which rescales O, already holding PV(j-1)), S(j+1) with the
+  // exponentials. r0, r1, r2: byte offsets of ring slots (j - tb) % 3, +1, +2.
+  const int need_lo = jlo - 1;
+  const uint32_t need_n = jlo < jhi ? (uint32_t)(jhi - jlo + 2) : 0u;
+  const uint32_t full_n = fhi > flo ? (uint32_t)(fhi - flo) : 0u;
+  uint32_t r0 = 0, r1 = TILEB, r2 = 2 * TILEB;
+  uint32_t k_soff = (uint32_t)((tb + 3) * BN) * k_rowb;
+  uint32_t v_soff = (uint32_t)((tb + 1) * BN) * v_rowb;
+
+  // V slot 2 stands for V(tb-1), read against P = 0 by the first step: zero it
+#pragma unroll
+  for (int c = tid * 16; c < TILEB; c += NT * 16) *(i32x4*)(vring + 2 * TILEB + c) = i32x4{};
+  if (tb < te) {
+    dma(k_d, kgoff, (uint32_t)(tb * BN) * k_rowb, kring_a);
+    if (tb + 1 < te) dma(k_d, kgoff, (uint32_t)((tb + 1) * BN) * k_rowb, kring_a + TILEB);
+    dma(v_d, vgoff, (uint32_t)(tb * BN) * v_rowb, vring_a);
+    if (tb + 2 < te) dma(k_d, kgoff, (uint32_t)((tb + 2) * BN) * k_rowb, kring_a + 2 * TILEB);
+  }
+  const int pro_pending = tb < te ? CH * (1 + (int)(tb + 2 < te)) : 0;
+  barrier_keep(pro_pending);
+  f32x16 sa[KB], sb[KB];
+  int pa[8], pb[8];      // e4m3 codes of 2^8 p, in accumulator order (byte kb*16 + r)
+#pragma unroll
+  for (int w = 0; w < 8; ++w) pa[w] = pb[w] = 0;
+  {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sa[kb] = f32x16{};
+#pragma unroll
+    for (int e = 0; e < NSM; ++e) sa[e % KB] = mfma_fp8(k_operand(kring_a, e), qop[e / KB], sa[e % KB]);
+  }
+  barrier_keep(pro_pending);   // every wave has read K(tb) before step tb refills its slot
+
+  auto step = [&](int j, f32x16 (&sc)[KB], f32x16 (&sn)[KB], const int (&pp)[8], int (&pc)[8]) {
+    const bool k3 = j + 3 < te, v1 = j + 1 < te;
+    if (k3) dma(k_d, kgoff, k_soff, kring_a + r0);
+    if (v1) dma(v_d, vgoff, v_soff, vring_a + r1);
+    if ((uint32_t)(j - need_lo) < need_n) {
+      if (!((uint32_t)(j - flo) < full_n)) mask_tile(sc, j);
+      i32x8 vop[DB], kop[NSM];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) vop[db] = v_operand(vring_a + r2, db);      // V(j-1)
+#pragma unroll
+      for (int e = 0; e < NSM; ++e) kop[e] = k_operand(kring_a + r1, e);         // K(j+1)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) sn[kb] = f32x16{};
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      const i32x8 pop = i32x8{pp[0], pp[1], pp[2], pp[3], pp[4], pp[5], pp[6], pp[7]};
+      // first half: PV(j-1) and the row max
+      __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_sched_barrier(0);
+      float mx = sc[0][0];
+      constexpr int MAXPER = KB * 16 / DB;   // max-ed values per PV MFMA
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const uint32_t vbase = opaque_vbase(lds_addr_of(vs) + voff[db]);
-        i32x2 part[4];
+        o[db] = mfma_fp8(vop[db], pop, o[db]);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int pr = 0; pr < 2; ++pr)
-            part[kb * 2 + pr] = lds_read_tr8(vbase + (kb * 32 + pr * 8) * ROWB);
-        vop[db] = i32x8{part[0][0], part[0][1], part[1][0], part[1][1], part[2][0], part[2][1], part[3][0], part[3][1]};
+        for (int q = db * MAXPER; q < (db + 1) * MAXPER; ++q) mx = fmaxf(mx, sc[q / 16][q % 16]);
+        asm volatile("" ::"v"(mx));
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (tile_partial(t)) {
-        const int jl = j0 + hl * 4 - lo_i;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = jl + kb * 32 + (r >> 2) * 8 + (r & 3);
-            sc[kb][r] = (uint32_t)j < span_i ? sc[kb][r] : -INFINITY;
-          }
-      }
-      // row max, lazily moved reference (p <= 2^0.8 keeps 2^8 p inside the e4m3 range)
-      float mx = sc[0][0];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+      __builtin_amdgcn_s_setprio(0);
+      // reference update (lazy: p <= 2^0.8 keeps 2^8 p inside the e4m3 range)
       mx = pair_max(mx) * c2;
       const float m_new = mx > m + kTau8 ? mx : m;
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+      if (__builtin_amdgcn_ballot_w64(m_new != m)) {
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
         l *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[db] *= alpha;
       }
       m = m_new;
-      // 2^8 p, its fp32 sum, and its e4m3 codes in accumulator order (byte kb*16 + r)
-      const float shift = kPShiftLog2 - m_use;
+      // second half: S(j+1) and 2^8 p = exp2(s c - m + 8), its fp32 sum and its e4m3 codes
+      const float shift = kPShiftLog2 - m;
       float rs = 0.f;
-      int pw[8];
+      __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_sched_barrier(0);
+      constexpr int WPER = 8 / NSM;          // code words per S MFMA
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+      for (int e = 0; e < NSM; ++e) {
+        sn[e % KB] = mfma_fp8(kop[e], qop[e / KB], sn[e % KB]);
 #pragma unroll
-        for (int w4 = 0; w4 < 4; ++w4) {
+        for (int wq = e * WPER; wq < (e + 1) * WPER; ++wq) {
+          const int kb = wq / 4, w4 = wq % 4;
           float p[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][4 * w4 + e], c2, shift));
-            rs += p[e];
+          for (int u = 0; u < 4; ++u) {
+            p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][4 * w4 + u], c2, shift));
+            rs += p[u];
           }
-          int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-          pw[kb * 4 + w4] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
+          const int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+          pc[wq] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
+          asm volatile("" ::"v"(pc[wq]), "v"(rs));
         }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_setprio(0);
       l += rs;
-      const i32x8 pop = i32x8{pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] = mfma_fp8(vop[db], pop, o[db]);
     }
-    barrier_keep(CH * ((int)k3 + (int)v2));
+    barrier_keep(CH * ((int)k3 + (int)v1));
+    const uint32_t rt = r0;
+    r0 = r1;
+    r1 = r2;
+    r2 = rt;
+    k_soff = __builtin_amdgcn_readfirstlane(k_soff + BN * k_rowb);
+    v_soff = __builtin_amdgcn_readfirstlane(v_soff + BN * v_rowb);
   };
 
-  for (int t = tb; t < te; t += 2) {
-    step(t, sa, sb);
-    if (t + 1 < te) step(t + 1, sb, sa);
+  // steps tb .. te; the last one only drains PV(te-1)
+  for (int t = tb;; t += 2) {
+    step(t, sa, sb, pb, pa);
+    if (t + 1 > te) break;
+    step(t + 1, sb, sa, pa, pb);
+    if (t + 2 > te) break;
   }
 
   // epilogue: O * dv / l (both carry the 2^8 shift), lse = (m + log2(l / 2^8)) * ln 2
