@@ -78,12 +78,24 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_fp8_kernel(FwdArgs a) {
   const int hl = lane >> 5;
   const int l32 = lane & 31;
 
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = L / a.num_q_tiles;
-  int qt = L - bh * a.num_q_tiles;
-  if (a.causal) qt = a.num_q_tiles - 1 - qt;
-  const int b = bh / a.Hq;
-  const int h = bh - b * a.Hq;
+  // workgroup order as in the 16-bit kernel: longest causal tiles first, K/V-head groups per XCD
+  int b, h, qt;
+  if (a.causal) {
+    const int n_bh = gridDim.x / a.num_q_tiles;
+    const int rank = blockIdx.x / n_bh;
+    const int idx = blockIdx.x - rank * n_bh;
+    const int hkv = a.Hq / a.group, n_kvh = n_bh / a.group;
+    const int g = idx / n_kvh, kvh = idx - g * n_kvh;
+    b = kvh / hkv;
+    h = (kvh - b * hkv) * a.group + g;
+    qt = a.num_q_tiles - 1 - rank;
+  } else {
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    const int bh = L / a.num_q_tiles;
+    qt = L - bh * a.num_q_tiles;
+    b = bh / a.Hq;
+    h = bh - b * a.Hq;
+  }
   const int hk = h / a.group;
   const int q0 = qt * BM;
 
@@ -121,16 +133,9 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_fp8_kernel(FwdArgs a) {
   const int hi_i = clamp_key(key_hi(ms, my_row));
   const uint32_t span_i = hi_i >= lo_i ? (uint32_t)(hi_i - lo_i + 1) : 0u;
 
-  // Q operands (B operand of S^T): row my_row, head-dim bytes ks*64 + hl*32 .. +31
+  // Q operands (B operand of S^T): row my_row, head-dim bytes ks*64 + hl*32 .. +31; loaded in
+  // the prologue behind the first K/V tile loads
   i32x8 qop[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const uint32_t off = (uint32_t)my_row * q_rowb + ks * 64 + hl * 32;
-    const i32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(q_r, off, 0, 0);
-    const i32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(q_r, off + 16, 0, 0);
-    qop[ks] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): Q has landed before the pipelined loop
 
   // HBM -> LDS: slot position P = (i * NT + tid) * 16 holds LDS row P / ROWB, physical chunk
   // (P % ROWB) / 16. K rows are in key order; V rows in the permuted order above.
@@ -233,8 +238,15 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_fp8_kernel(FwdArgs a) {
     dma(v_d, vgoff, (uint32_t)(tb * BN) * v_rowb, vring_a);
     if (tb + 2 < te) dma(k_d, kgoff, (uint32_t)((tb + 2) * BN) * k_rowb, kring_a + 2 * TILEB);
   }
-  const int pro_pending = tb < te ? CH * (1 + (int)(tb + 2 < te)) : 0;
-  barrier_keep(pro_pending);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint32_t off = (uint32_t)my_row * q_rowb + ks * 64 + hl * 32;
+    const i32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(q_r, off, 0, 0);
+    const i32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(q_r, off + 16, 0, 0);
+    qop[ks] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): Q and the first tiles have landed
+  barrier_keep(0);
   f32x16 sa[KB], sb[KB];
   int pa[8], pb[8];      // e4m3 codes of 2^8 p, in accumulator order (byte kb*16 + r)
 #pragma unroll
@@ -245,7 +257,7 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_fp8_kernel(FwdArgs a) {
 #pragma unroll
     for (int e = 0; e < NSM; ++e) sa[e % KB] = mfma_fp8(k_operand(kring_a, e), qop[e / KB], sa[e % KB]);
   }
-  barrier_keep(pro_pending);   // every wave has read K(tb) before step tb refills its slot
+  barrier_keep(0);   // every wave has read K(tb) before step tb refills its slot
 
   auto step = [&](int j, f32x16 (&sc)[KB], f32x16 (&sn)[KB], const int (&pp)[8], int (&pc)[8]) {
     const bool k3 = j + 3 < te, v1 = j + 1 < te;
