@@ -29,6 +29,35 @@ __device__ inline int xcd_remap(int id, int n) {
   return xcd * per + (xcd < rem ? xcd : rem) + k;
 }
 
+// Which (batch, query head, query tile) workgroup `id` of a launch of n computes. Blocks are dealt
+// round-robin over the 8 XCDs; xcd_remap turns that into one contiguous range of the sequence
+// below per XCD. Heads are enumerated batch-major, and inside a batch the query heads sharing a
+// K/V head are consecutive. Without a causal mask the sequence is head by head (a head's K/V
+// then stays in one XCD's L2). Under a causal mask query tiles differ in length by up to the
+// number of tiles, so the sequence goes by chunks of kChunk heads (one K/V head under 4-way
+// GQA), longest tiles of the chunk first: the chunks in flight on an XCD keep its L2 working
+// set small, and the longest work of each chunk starts first, which keeps the launch's tail
+// short.
+__device__ inline void schedule_block(int id, int n, int num_q_tiles, int Hq, bool causal, int* b, int* h, int* qt) {
+  constexpr int kChunk = 4;
+  const int L = xcd_remap(id, n);
+  const int n_bh = n / num_q_tiles;
+  int bh;
+  if (causal && n_bh % kChunk == 0) {
+    const int per = kChunk * num_q_tiles;
+    const int chunk = L / per, r = L - chunk * per;
+    const int rank = r / kChunk;
+    bh = chunk * kChunk + (r - rank * kChunk);
+    *qt = num_q_tiles - 1 - rank;
+  } else {
+    bh = L / num_q_tiles;
+    *qt = L - bh * num_q_tiles;
+    if (causal) *qt = num_q_tiles - 1 - *qt;
+  }
+  *b = bh / Hq;
+  *h = bh - *b * Hq;
+}
+
 // Value of x held by lane l ^ 32, combined with x: max or sum over the lane pair.
 __device__ inline float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

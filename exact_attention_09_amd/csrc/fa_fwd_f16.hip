@@ -70,27 +70,7 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
 
   // ---- which (batch, head, query tile) this workgroup computes
   int b, h, qt;
-  if (a.causal) {
-    // Causal query tiles differ in length by up to the number of tiles; all heads' tiles of one
-    // length run before any shorter ones (longest first, which keeps the tail of the launch
-    // short). Within a length, consecutive workgroups (dealt round-robin over the 8 XCDs) take
-    // consecutive K/V heads, so the query heads sharing a K/V head land on the same XCD.
-    const int n_bh = gridDim.x / a.num_q_tiles;
-    const int rank = blockIdx.x / n_bh;
-    const int idx = blockIdx.x - rank * n_bh;
-    const int hkv = a.Hq / a.group, n_kvh = n_bh / a.group;
-    const int g = idx / n_kvh, kvh = idx - g * n_kvh;
-    b = kvh / hkv;
-    h = (kvh - b * hkv) * a.group + g;
-    qt = a.num_q_tiles - 1 - rank;
-  } else {
-    // equal tiles: a head's tiles stay together on one XCD, whose L2 then holds its K/V
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = L / a.num_q_tiles;
-    qt = L - bh * a.num_q_tiles;
-    b = bh / a.Hq;
-    h = bh - b * a.Hq;
-  }
+  schedule_block(blockIdx.x, gridDim.x, a.num_q_tiles, a.Hq, a.causal != 0, &b, &h, &qt);
   const int hk = h / a.group;                    // MQA/GQA: K/V head of this query head
   const int q0 = qt * BM;
 

@@ -78,24 +78,9 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_fp8_kernel(FwdArgs a) {
   const int hl = lane >> 5;
   const int l32 = lane & 31;
 
-  // workgroup order as in the 16-bit kernel: longest causal tiles first, K/V-head groups per XCD
+  // which (batch, head, query tile) this workgroup computes
   int b, h, qt;
-  if (a.causal) {
-    const int n_bh = gridDim.x / a.num_q_tiles;
-    const int rank = blockIdx.x / n_bh;
-    const int idx = blockIdx.x - rank * n_bh;
-    const int hkv = a.Hq / a.group, n_kvh = n_bh / a.group;
-    const int g = idx / n_kvh, kvh = idx - g * n_kvh;
-    b = kvh / hkv;
-    h = (kvh - b * hkv) * a.group + g;
-    qt = a.num_q_tiles - 1 - rank;
-  } else {
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const int bh = L / a.num_q_tiles;
-    qt = L - bh * a.num_q_tiles;
-    b = bh / a.Hq;
-    h = bh - b * a.Hq;
-  }
+  schedule_block(blockIdx.x, gridDim.x, a.num_q_tiles, a.Hq, a.causal != 0, &b, &h, &qt);
   const int hk = h / a.group;
   const int q0 = qt * BM;
 
