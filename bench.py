@@ -12,8 +12,10 @@ resident in device memory before the timed region. Prints one JSON line.
 
 Also reported:
   * roofline — the kernel's achieved TFLOP/s against MI355X's dense MFMA peak for its dtype,
-    from HIP events recorded around each launch on the launch stream; HBM traffic from the
-    committed rocprofv3 counter summary when it was taken on the current kernel source;
+    from HIP events recorded around each launch on the launch stream (mean and median per
+    launch); HBM traffic from the committed rocprofv3 counter summary when it was taken on the
+    current kernel source;
+  * cold_cache — the median launch after 512 MiB of writes have evicted L2 and the MALL;
   * cpu_baseline — the fp64 CPU oracle timed on this host on a bounded sample of the same
     workload (whole heads), scaled to the same metric.
 """
@@ -147,6 +149,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                     help="oracle time budget on the host; 0 skips the CPU baseline")
+    ap.add_argument("--cold-launches", type=int, default=10,
+                    help="launches timed after writing 512 MiB (cold L2/MALL); 0 skips them")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of attention, run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -211,7 +215,26 @@ def main():
     wall = time.perf_counter() - t0
     kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     avg_kernel_s = sum(kernel_ms) / len(kernel_ms) / 1e3
+    med_kernel_s = sorted(kernel_ms)[len(kernel_ms) // 2] / 1e3
     ms_per_step = wall / args.steps * 1e3
+
+    # Cold-cache variant: 512 MiB written between launches evicts L2 and the MALL.
+    cold = None
+    if args.cold_launches > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        cold_ms = []
+        for i in range(args.cold_launches):
+            flush.fill_(i & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            e1.synchronize()
+            cold_ms.append(e0.elapsed_time(e1))
+        del flush
+        cold_med = sorted(cold_ms)[len(cold_ms) // 2] / 1e3
+        cold = {"launches": args.cold_launches, "kernel_median_us": round(cold_med * 1e6, 3),
+                "TFLOPs": round(metric_flops(w) / cold_med / 1e12, 2)}
 
     flops = metric_flops(w)
     value = flops / (ms_per_step / 1e3) / 1e12
@@ -239,9 +262,12 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel_avg_us": round(avg_kernel_s * 1e6, 3),
+                     "kernel_median_us": round(med_kernel_s * 1e6, 3),
                      "algorithmic_bytes": algorithmic_bytes(w),
                      "algorithmic_GBps": round(algorithmic_bytes(w) / avg_kernel_s / 1e9, 1)},
     }
+    if cold is not None:
+        rec["cold_cache"] = cold
     if args.cpu_baseline_seconds > 0:
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v, descale, args.cpu_baseline_seconds)
     print(json.dumps(rec), flush=True)
