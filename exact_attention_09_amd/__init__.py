@@ -1,12 +1,12 @@
-"""libfa355: the FlashAttention forward pass on AMD MI355X (gfx950).
+"""libfa355: the FlashAttention forward pass (and its backward pass) on AMD MI355X (gfx950).
 
 The computation runs in hand-written HIP kernels behind the C ABI of ``include/fa355.h``
 (``libfa355.so``, built in-tree by ``python -m exact_attention_09_amd.build``). This package is
 the thin Python binding used by the tests and the benchmark; importing it does not load the
 library — the first call does, and raises if the library is missing.
 """
-from .fa355 import (EXPORTED, FA_BF16, FA_F16, FA_FP8_E4M3, LIB_PATH, FaError, fwd, fwd_raw, kv_tile_range, load,
-                    plan, status_str)
+from .fa355 import (EXPORTED, FA_BF16, FA_F16, FA_FP8_E4M3, LIB_PATH, FaError, bwd, bwd_raw, fwd, fwd_raw,
+                    kv_tile_range, load, plan, status_str)
 
-__all__ = ["EXPORTED", "FA_BF16", "FA_F16", "FA_FP8_E4M3", "LIB_PATH", "FaError", "fwd", "fwd_raw", "kv_tile_range",
-           "load", "plan", "status_str"]
+__all__ = ["EXPORTED", "FA_BF16", "FA_F16", "FA_FP8_E4M3", "LIB_PATH", "FaError", "bwd", "bwd_raw", "fwd", "fwd_raw",
+           "kv_tile_range", "load", "plan", "status_str"]

@@ -196,4 +196,58 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* out, float* 
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, float* delta, int B, int Nq, int Nk, int Hq, int Hkv, int D,
+                 const fa_bwd_strides* s, float softmax_scale, int causal, int window_left, int window_right,
+                 fa_dtype dtype, hipStream_t stream) {
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !delta || !s) return FA_ERR_NULL;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  fa_status st = check_sizes(B, Nq, Nk, Hq, Hkv, D, window_left, window_right, dtype);
+  if (st != FA_OK) return st;
+  if (!finite_pos(softmax_scale)) return FA_ERR_SCALE;
+  const int64_t str[24] = {s->q_b,  s->q_n,  s->q_h,  s->k_b,  s->k_n,  s->k_h,  s->v_b,  s->v_n,
+                           s->v_h,  s->o_b,  s->o_n,  s->o_h,  s->do_b, s->do_n, s->do_h, s->dq_b,
+                           s->dq_n, s->dq_h, s->dk_b, s->dk_n, s->dk_h, s->dv_b, s->dv_n, s->dv_h};
+  for (int i = 0; i < 24; ++i)
+    if (str[i] < 0 || (str[i] * 2) % 16 != 0) return FA_ERR_STRIDES;
+  // written tensors: rows and heads must not overlap
+  if ((Nq > 1 && s->dq_n < D) || (Hq > 1 && s->dq_h < D) || (B > 1 && s->dq_b < D)) return FA_ERR_STRIDES;
+  if ((Nk > 1 && (s->dk_n < D || s->dv_n < D)) || (Hkv > 1 && (s->dk_h < D || s->dv_h < D)) ||
+      (B > 1 && (s->dk_b < D || s->dv_b < D)))
+    return FA_ERR_STRIDES;
+  const void* ptrs[9] = {q, k, v, out, dout, dq, dk, dv, nullptr};
+  for (int i = 0; i < 8; ++i)
+    if (!aligned16(ptrs[i])) return FA_ERR_STRIDES;
+  if (((uintptr_t)lse & 3u) || ((uintptr_t)delta & 3u)) return FA_ERR_STRIDES;
+  if ((int64_t)B * Hq * Nq >= ((int64_t)1 << 31) / 16) return FA_ERR_SHAPE;
+
+  fa::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = out; a.dout = dout; a.lse = lse;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.delta = delta;
+  a.B = B; a.Nq = Nq; a.Nk = Nk; a.Hq = Hq; a.Hkv = Hkv; a.group = Hq / Hkv;
+  a.causal = causal ? 1 : 0;
+  a.wl = window_left;
+  a.wr = window_right;
+  a.num_q_tiles = (Nq + fa::kBwdQRows - 1) / fa::kBwdQRows;
+  a.num_k_tiles = (Nk + fa::kBwdKRows - 1) / fa::kBwdKRows;
+  a.q_b = s->q_b; a.q_n = s->q_n; a.q_h = s->q_h;
+  a.k_b = s->k_b; a.k_n = s->k_n; a.k_h = s->k_h;
+  a.v_b = s->v_b; a.v_n = s->v_n; a.v_h = s->v_h;
+  a.o_b = s->o_b; a.o_n = s->o_n; a.o_h = s->o_h;
+  a.do_b = s->do_b; a.do_n = s->do_n; a.do_h = s->do_h;
+  a.dq_b = s->dq_b; a.dq_n = s->dq_n; a.dq_h = s->dq_h;
+  a.dk_b = s->dk_b; a.dk_n = s->dk_n; a.dk_h = s->dk_h;
+  a.dv_b = s->dv_b; a.dv_n = s->dv_n; a.dv_h = s->dv_h;
+  if (!span_ok(Nq, s->q_n, D, 2, &a.q_bytes) || !span_ok(Nk, s->k_n, D, 2, &a.k_bytes) ||
+      !span_ok(Nk, s->v_n, D, 2, &a.v_bytes) || !span_ok(Nq, s->o_n, D, 2, &a.o_bytes) ||
+      !span_ok(Nq, s->do_n, D, 2, &a.do_bytes) || !span_ok(Nq, s->dq_n, D, 2, &a.dq_bytes) ||
+      !span_ok(Nk, s->dk_n, D, 2, &a.dk_bytes) || !span_ok(Nk, s->dv_n, D, 2, &a.dv_bytes))
+    return FA_ERR_TOO_LARGE;
+  if ((int64_t)B * Hkv * a.num_k_tiles >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+  a.scale = softmax_scale;
+  a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  const hipError_t e = fa::launch_bwd(a, D, dtype, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 }  // extern "C"

@@ -1,0 +1,495 @@
+// fa_bwd_f16.hip — FlashAttention backward pass for fp16 / bf16 on gfx950 (MI355X).
+//
+// The method recomputes attention from the saved log-sum-exp instead of storing the score
+// matrix ("Flash Attention - Fast Memory-Efficient Attention", skill page, Quick start: IO-aware
+// tiling and recomputation). For an upstream gradient dout of the output, with
+// p_ij = exp(s_ij - lse_i), s = scale * q.k over admitted pairs:
+//     dv_j = sum_i p_ij dout_i                 dp_ij = dout_i . v_j
+//     ds_ij = p_ij (dp_ij - delta_i),          delta_i = dout_i . out_i  (= sum_j p_ij dp_ij)
+//     dq_i = scale sum_j ds_ij k_j             dk_j = scale sum_i ds_ij q_i
+// and a K/V head shared by several query heads (MQA/GQA) receives the sum of their terms.
+//
+// Three kernels, none with atomics (the result is deterministic):
+//  * delta: rowsum(dout * out) per query row, into a caller-provided fp32 workspace;
+//  * dq: one workgroup per (batch, query head, 128 query rows), walking the K/V tiles the rows
+//    attend to. Lanes own queries, as in the forward kernel: S^T = K Q^T and dP^T = V dO^T come
+//    out with one query per lane, so lse_i and delta_i are per-lane scalars, and dS^T is the B
+//    operand of dQ^T = K^T dS^T with K^T read by ds_read_b64_tr_b16 in the matching key order;
+//  * dk/dv: one workgroup per (batch, K/V head, 128 keys), walking the query tiles (of every
+//    query head that reads this K/V head) that attend to its keys. Lanes own keys: S = Q K^T and
+//    dP = dO V^T come out with one key per lane; P and dS are the B operands of
+//    dV^T = dO^T P and dK^T = Q^T dS, with dO^T and Q^T read by transpose reads.
+// Tiles stream HBM -> LDS by 128-bit LDS-direct loads into two-slot rings; every tile uses the
+// row swizzle of the forward kernel's K tile (conflict-free row reads); transpose reads pick the
+// swizzle of each 8-row group.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_device.hpp"
+#include "fa_f16_common.hpp"
+#include "fa_kernels.hpp"
+#include "fa_mask.hpp"
+
+namespace fa {
+
+template <class TR>
+__device__ inline void unpack2(uint32_t w, float& x, float& y) {
+  if constexpr (TR::kDtype == 0) {
+    const f16x2 h = __builtin_bit_cast(f16x2, w);
+    x = (float)h[0];
+    y = (float)h[1];
+  } else {
+    x = __uint_as_float(w << 16);
+    y = __uint_as_float(w & 0xFFFF0000u);
+  }
+}
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// ---------------------------------------------------------------------------------------------
+// delta[b, h, i] = sum_d dout[b, i, h, d] * out[b, i, h, d]; D/8 lanes per row, 16 bytes each.
+template <class TR, int D>
+__global__ void __launch_bounds__(256) fa_bwd_delta_kernel(BwdArgs a) {
+  constexpr int LPR = D / 8;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid / LPR;
+  const int part = (int)(gid % LPR);
+  const int64_t nrows = (int64_t)a.B * a.Hq * a.Nq;
+  float s = 0.f;
+  if (row < nrows) {
+    const int i = (int)(row % a.Nq);
+    const int64_t bh = row / a.Nq;
+    const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+    const i32x4 o = *(const i32x4*)((const char*)a.o + (b * a.o_b + i * a.o_n + h * a.o_h + part * 8) * 2);
+    const i32x4 d = *(const i32x4*)((const char*)a.dout + (b * a.do_b + i * a.do_n + h * a.do_h + part * 8) * 2);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float o0, o1, d0, d1;
+      unpack2<TR>((uint32_t)o[e], o0, o1);
+      unpack2<TR>((uint32_t)d[e], d0, d1);
+      s = __builtin_fmaf(o0, d0, __builtin_fmaf(o1, d1, s));
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if (row < nrows && part == 0) a.delta[row] = s;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Shared pieces of the two tile kernels: the LDS tile layout (row-major, 16-byte chunks XOR-ed by
+// k_swz of the row) and the per-lane offsets of its row reads and transpose reads.
+template <int D>
+struct BwdTile {
+  static constexpr int ROWB = D * 2;
+  static constexpr int TILEB = 64 * ROWB;     // 64 rows
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  // Row read (A or B operand with the head dimension as k): row r (0..31 of a 32-row block),
+  // k-slots ks*16 + hl*8 .. +7.
+  __device__ static int row_off(int r, int ks, int hl) { return r * ROWB + (((2 * ks + hl) ^ k_swz<ROWB>(r)) << 4); }
+  // Transpose read (A operand with the rows as k): for 16-lane group g16 and lane s16 = 4 tr + tc,
+  // rows 4 (g16 >> 1) + tr (+ 8 e8), columns db*32 + (g16 & 1)*16 + 4 tc .. +3. Adding 16 or 32
+  // rows keeps the swizzle, adding 8 changes it, so each column block has two offsets.
+  __device__ static int tr_off(int lane, int db, int e8) {
+    const int g16 = lane >> 4, s16 = lane & 15, tr = s16 >> 2, tc = s16 & 3;
+    const int row = 4 * (g16 >> 1) + tr;
+    const int chunk = db * 4 + (g16 & 1) * 2 + (tc >> 1);
+    return row * ROWB + ((chunk ^ k_swz<ROWB>(row + 8 * e8)) << 4) + (tc & 1) * 8;
+  }
+};
+
+// A operand of a product whose k runs over 16 tile rows (block of 32 rows kb, half 'half'):
+// rows kb*32 + half*16 + (t / 4) * 8 + (l / 32) * 4 + t % 4 for k-slot (l / 32) * 8 + t, i.e. the
+// order in which a 32x32 accumulator holds its rows, so that an accumulator packed to 16 bits is
+// the matching B operand.
+template <int D>
+__device__ inline i32x4 tr_operand(uint32_t slot, const int (&toff)[D / 32][2], int kb, int half, int db) {
+  constexpr int ROWB = D * 2;
+  const uint32_t p0 = opaque_vbase(slot + toff[db][0]) + (kb * 32 + half * 16) * ROWB;
+  const uint32_t p1 = opaque_vbase(slot + toff[db][1]) + (kb * 32 + half * 16 + 8) * ROWB;
+  const i32x2 v0 = lds_read_tr16(p0), v1 = lds_read_tr16(p1);
+  return i32x4{v0[0], v0[1], v1[0], v1[1]};
+}
+
+// ---------------------------------------------------------------------------------------------
+template <class TR, int D>
+__global__ void __launch_bounds__(256) fa_bwd_dq_kernel(BwdArgs a) {
+  using T = BwdTile<D>;
+  constexpr int NT = 256, BM = kBwdQRows, BN = 64, ES = 2;
+  constexpr int ROWB = T::ROWB, TILEB = T::TILEB, KS = T::KS, DB = T::DB, KB = BN / 32;
+  constexpr int CH = BN * (D / 8) / NT;     // 16-byte loads per thread per tile
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILEB];   // [K0 K1 | V0 V1]
+  char* const kring = smem;
+  char* const vring = smem + 2 * TILEB;
+
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int b, h, qt;
+  schedule_block(blockIdx.x, gridDim.x, a.num_q_tiles, a.Hq, a.causal != 0, &b, &h, &qt);
+  const int hk = h / a.group;
+  const int q0 = qt * BM;
+  const MaskSpec ms{a.Nq, a.Nk, a.causal, a.wl, a.wr};
+
+  const char* kbp = (const char*)a.k + (b * a.k_b + hk * a.k_h) * ES;
+  const char* vbp = (const char*)a.v + (b * a.v_b + hk * a.v_h) * ES;
+  const __amdgpu_buffer_rsrc_t q_r = make_rsrc((const char*)a.q + (b * a.q_b + h * a.q_h) * ES, a.q_bytes);
+  const __amdgpu_buffer_rsrc_t do_r = make_rsrc((const char*)a.dout + (b * a.do_b + h * a.do_h) * ES, a.do_bytes);
+  const __amdgpu_buffer_rsrc_t dq_r = make_rsrc((char*)a.dq + (b * a.dq_b + h * a.dq_h) * ES, a.dq_bytes);
+  const uint32_t k_rowb = (uint32_t)(a.k_n * ES), v_rowb = (uint32_t)(a.v_n * ES);
+
+  const int wg_last = min(q0 + BM, a.Nq) - 1;
+  int tb, te;
+  tile_range(ms, q0, wg_last, BN, &tb, &te);
+  const int w0 = q0 + wave * 32;
+  const bool wave_live = w0 < a.Nq;
+  const int w1 = min(w0 + 31, a.Nq - 1);
+  auto clamp_key = [&](int64_t x) { return (int)(x < -1 ? -1 : (x > a.Nk ? a.Nk : x)); };
+  const int wlo0 = __builtin_amdgcn_readfirstlane(clamp_key(key_lo(ms, w0)));
+  const int wlo1 = __builtin_amdgcn_readfirstlane(clamp_key(key_lo(ms, w1)));
+  const int whi0 = __builtin_amdgcn_readfirstlane(clamp_key(key_hi(ms, w0)));
+  const int whi1 = __builtin_amdgcn_readfirstlane(clamp_key(key_hi(ms, w1)));
+  const int my_row = w0 + l32;
+  const int lo_i = clamp_key(key_lo(ms, my_row));
+  const int hi_i = clamp_key(key_hi(ms, my_row));
+  const uint32_t span_i = hi_i >= lo_i ? (uint32_t)(hi_i - lo_i + 1) : 0u;
+
+  // this lane's query row: Q and dO as B operands, lse (base 2) and delta
+  i32x4 qop[KS], dop[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qop[ks] = __builtin_amdgcn_raw_buffer_load_b128(q_r, (uint32_t)my_row * (uint32_t)(a.q_n * ES) + (ks * 16 + hl * 8) * ES, 0, 0);
+    dop[ks] = __builtin_amdgcn_raw_buffer_load_b128(do_r, (uint32_t)my_row * (uint32_t)(a.do_n * ES) + (ks * 16 + hl * 8) * ES, 0, 0);
+  }
+  float lse2 = INFINITY, delta = 0.f;   // rows past the end or with no key: p = 0
+  if (my_row < a.Nq) {
+    const int64_t r = ((int64_t)b * a.Hq + h) * a.Nq + my_row;
+    const float l = a.lse[r];
+    if (l > -INFINITY) lse2 = l * kLog2e;
+    delta = a.delta[r];
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+
+  uint32_t kgoff[CH], vgoff[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int pos = (i * NT + tid) * 16, row = pos / ROWB, pc = (pos % ROWB) / 16;
+    kgoff[i] = (uint32_t)row * k_rowb + ((pc ^ k_swz<ROWB>(row)) << 4);
+    vgoff[i] = (uint32_t)row * v_rowb + ((pc ^ k_swz<ROWB>(row)) << 4);
+  }
+  const BufDesc k_d = make_desc(kbp, a.k_bytes), v_d = make_desc(vbp, a.v_bytes);
+  const uint32_t kring_a = lds_addr_of(kring), vring_a = lds_addr_of(vring);
+  auto dma = [&](const BufDesc& d, const uint32_t* goff, uint32_t soff, uint32_t lds) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) dma16(d, goff[i], soff, lds + wave * 64 * 16 + i * NT * 16);
+  };
+  auto barrier_keep = [&](int pending) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (pending >= 2 * CH) __builtin_amdgcn_s_waitcnt(0x0070 | (2 * CH));
+    else __builtin_amdgcn_s_waitcnt(0x0070);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+  int roff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = T::row_off(l32, ks, hl);
+  int toff[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int e8 = 0; e8 < 2; ++e8) toff[db][e8] = T::tr_off(lane, db, e8);
+
+  const float c2 = a.scale_log2;
+  f32x16 dq[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
+
+  if (tb < te) {
+    dma(k_d, kgoff, (uint32_t)(tb * BN) * k_rowb, kring_a);
+    dma(v_d, vgoff, (uint32_t)(tb * BN) * v_rowb, vring_a);
+  }
+  for (int t = tb; t < te; ++t) {
+    const uint32_t s = (uint32_t)((t - tb) & 1) * TILEB;
+    const bool more = t + 1 < te;
+    if (more) {
+      dma(k_d, kgoff, (uint32_t)((t + 1) * BN) * k_rowb, kring_a + (TILEB - s));
+      dma(v_d, vgoff, (uint32_t)((t + 1) * BN) * v_rowb, vring_a + (TILEB - s));
+    }
+    barrier_keep(more ? 2 * CH : 0);   // tile t landed for every wave
+    const bool live = wave_live && t * BN + BN - 1 >= wlo0 && t * BN <= whi1;
+    if (live) {
+      f32x16 st[KB], dpt[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) st[kb] = dpt[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t kbase = opaque_vbase(kring_a + s + roff[ks]);
+        const uint32_t vbase = opaque_vbase(vring_a + s + roff[ks]);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          st[kb] = TR::mfma(lds_read_b128(kbase + kb * 32 * ROWB), qop[ks], st[kb]);
+          dpt[kb] = TR::mfma(lds_read_b128(vbase + kb * 32 * ROWB), dop[ks], dpt[kb]);
+        }
+      }
+      if (!(wlo1 <= t * BN && t * BN + BN - 1 <= whi0)) {
+        const int jl = t * BN + hl * 4 - lo_i;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = jl + kb * 32 + (r >> 2) * 8 + (r & 3);
+            st[kb][r] = (uint32_t)j < span_i ? st[kb][r] : -INFINITY;
+          }
+      }
+      // ds^T = p (dp^T - delta), packed to the MFMA type in accumulator order
+      uint32_t dsk[KB][8];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][r], c2, -lse2));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][r + 1], c2, -lse2));
+          dsk[kb][r >> 1] = TR::pack(p0 * (dpt[kb][r] - delta), p1 * (dpt[kb][r + 1] - delta));
+        }
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const i32x4 dsop = i32x4{(int)dsk[kb][4 * half + 0], (int)dsk[kb][4 * half + 1], (int)dsk[kb][4 * half + 2],
+                                   (int)dsk[kb][4 * half + 3]};
+#pragma unroll
+          for (int db = 0; db < DB; ++db) dq[db] = TR::mfma(tr_operand<D>(kring_a + s, toff, kb, half, db), dsop, dq[db]);
+        }
+    }
+    barrier_keep(more ? 2 * CH : 0);   // every wave is done with slot s before it is refilled
+  }
+
+  if (!wave_live || my_row >= a.Nq) return;
+  const uint32_t dq_rowb = (uint32_t)(a.dq_n * ES);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const uint32_t w0v = TR::pack(dq[db][4 * q4 + 0] * a.scale, dq[db][4 * q4 + 1] * a.scale);
+      const uint32_t w1v = TR::pack(dq[db][4 * q4 + 2] * a.scale, dq[db][4 * q4 + 3] * a.scale);
+      __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)w0v, (int)w1v}, dq_r,
+                                            (uint32_t)my_row * dq_rowb + (db * 32 + q4 * 8 + hl * 4) * ES, 0, 0);
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+template <class TR, int D>
+__global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
+  using T = BwdTile<D>;
+  constexpr int NT = 256, BKV = kBwdKRows, BQ = 64, ES = 2;
+  constexpr int ROWB = T::ROWB, TILEB = T::TILEB, KS = T::KS, DB = T::DB, QB = BQ / 32;
+  constexpr int CH = BQ * (D / 8) / NT;
+  __shared__ __attribute__((aligned(16))) char smem[4 * TILEB];   // [Q0 Q1 | dO0 dO1]
+  char* const qring = smem;
+  char* const dring = smem + 2 * TILEB;
+
+  const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // (batch, K/V head, key tile); key tiles in increasing order: under a causal mask the first
+  // key tiles meet the most query tiles
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int bkv = L / a.num_k_tiles;
+  const int kt = L - bkv * a.num_k_tiles;
+  const int b = bkv / a.Hkv, hk = bkv - b * a.Hkv;
+  const int k0 = kt * BKV;
+  const int kw0 = k0 + wave * 32;
+  const int my_key = kw0 + l32;
+  const MaskSpec ms{a.Nq, a.Nk, a.causal, a.wl, a.wr};
+
+  const __amdgpu_buffer_rsrc_t k_r = make_rsrc((const char*)a.k + (b * a.k_b + hk * a.k_h) * ES, a.k_bytes);
+  const __amdgpu_buffer_rsrc_t v_r = make_rsrc((const char*)a.v + (b * a.v_b + hk * a.v_h) * ES, a.v_bytes);
+  const __amdgpu_buffer_rsrc_t dk_r = make_rsrc((char*)a.dk + (b * a.dk_b + hk * a.dk_h) * ES, a.dk_bytes);
+  const __amdgpu_buffer_rsrc_t dv_r = make_rsrc((char*)a.dv + (b * a.dv_b + hk * a.dv_h) * ES, a.dv_bytes);
+
+  // query rows that admit some key of this workgroup: [i_lo, i_hi]. Key j is admitted by row i
+  // iff lo(i) <= j <= hi(i); both bounds grow with i, so these rows form an interval.
+  const int k_last = min(k0 + BKV, a.Nk) - 1;
+  int i_lo = a.Nq, i_hi = -1;
+  {
+    // smallest i with hi(i) >= k0, largest i with lo(i) <= k_last (binary searches)
+    int lo = 0, hi = a.Nq;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (key_hi(ms, mid) >= k0) hi = mid; else lo = mid + 1;
+    }
+    i_lo = lo;
+    lo = -1;
+    hi = a.Nq - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (key_lo(ms, mid) <= k_last) lo = mid; else hi = mid - 1;
+    }
+    i_hi = lo;
+  }
+  i_lo = __builtin_amdgcn_readfirstlane(i_lo);
+  i_hi = __builtin_amdgcn_readfirstlane(i_hi);
+  const int ub = i_lo <= i_hi ? i_lo / BQ : 0, ue = i_lo <= i_hi ? i_hi / BQ + 1 : 0;
+  const int nu = ue - ub;                     // query tiles per query head
+  const int nsteps = nu * a.group;
+
+  // this lane's key: K and V as B operands
+  i32x4 kop[KS], vop[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kop[ks] = __builtin_amdgcn_raw_buffer_load_b128(k_r, (uint32_t)my_key * (uint32_t)(a.k_n * ES) + (ks * 16 + hl * 8) * ES, 0, 0);
+    vop[ks] = __builtin_amdgcn_raw_buffer_load_b128(v_r, (uint32_t)my_key * (uint32_t)(a.v_n * ES) + (ks * 16 + hl * 8) * ES, 0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  const uint32_t q_rowb = (uint32_t)(a.q_n * ES), do_rowb = (uint32_t)(a.do_n * ES);
+  uint32_t qgoff[CH], dgoff[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int pos = (i * NT + tid) * 16, row = pos / ROWB, pc = (pos % ROWB) / 16;
+    qgoff[i] = (uint32_t)row * q_rowb + ((pc ^ k_swz<ROWB>(row)) << 4);
+    dgoff[i] = (uint32_t)row * do_rowb + ((pc ^ k_swz<ROWB>(row)) << 4);
+  }
+  const uint32_t qring_a = lds_addr_of(qring), dring_a = lds_addr_of(dring);
+  auto dma = [&](const BufDesc& d, const uint32_t* goff, uint32_t soff, uint32_t lds) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) dma16(d, goff[i], soff, lds + wave * 64 * 16 + i * NT * 16);
+  };
+  auto barrier_keep = [&](int pending) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (pending >= 2 * CH) __builtin_amdgcn_s_waitcnt(0x0070 | (2 * CH));
+    else __builtin_amdgcn_s_waitcnt(0x0070);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+  // step n -> (query head h, query tile u)
+  auto head_of = [&](int n) { return hk * a.group + n / nu; };
+  auto tile_of = [&](int n) { return ub + n % nu; };
+  auto issue = [&](int n, uint32_t slot) {
+    const int hh = head_of(n), u = tile_of(n);
+    const BufDesc q_d = make_desc((const char*)a.q + (b * a.q_b + hh * a.q_h) * ES, a.q_bytes);
+    const BufDesc d_d = make_desc((const char*)a.dout + (b * a.do_b + hh * a.do_h) * ES, a.do_bytes);
+    dma(q_d, qgoff, (uint32_t)(u * BQ) * q_rowb, qring_a + slot);
+    dma(d_d, dgoff, (uint32_t)(u * BQ) * do_rowb, dring_a + slot);
+  };
+  int roff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) roff[ks] = T::row_off(l32, ks, hl);
+  int toff[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int e8 = 0; e8 < 2; ++e8) toff[db][e8] = T::tr_off(lane, db, e8);
+
+  // this wave's keys against a 32-query block starting at row i0: all admitted, none, or some
+  auto block_class = [&](int i0) {
+    const int i1 = min(i0 + 31, a.Nq - 1);
+    const int64_t j1 = min(kw0 + 31, a.Nk - 1);
+    if (kw0 >= a.Nk || i0 >= a.Nq) return 0;
+    if (key_hi(ms, i1) < kw0 || key_lo(ms, i0) > j1) return 0;
+    if (key_lo(ms, i1) <= kw0 && kw0 + 31 <= key_hi(ms, i0)) return 2;
+    return 1;
+  };
+
+  const float c2 = a.scale_log2;
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dk[db] = dv[db] = f32x16{};
+
+  if (nsteps > 0) issue(0, 0);
+  for (int n = 0; n < nsteps; ++n) {
+    const uint32_t s = (uint32_t)(n & 1) * TILEB;
+    const bool more = n + 1 < nsteps;
+    if (more) issue(n + 1, TILEB - s);
+    barrier_keep(more ? 2 * CH : 0);
+    const int hh = head_of(n), u = tile_of(n);
+    const float* lse_h = a.lse + ((int64_t)b * a.Hq + hh) * a.Nq;
+    const float* del_h = a.delta + ((int64_t)b * a.Hq + hh) * a.Nq;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int i0 = u * BQ + qb * 32;
+      const int cls = __builtin_amdgcn_readfirstlane(block_class(i0));
+      if (cls == 0) continue;
+      // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys (one key per lane)
+      f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sc = TR::mfma(lds_read_b128(opaque_vbase(qring_a + s + roff[ks]) + qb * 32 * ROWB), kop[ks], sc);
+        dp = TR::mfma(lds_read_b128(opaque_vbase(dring_a + s + roff[ks]) + qb * 32 * ROWB), vop[ks], dp);
+      }
+      // accumulator r holds query i0 + (r/4)*8 + hl*4 + r%4
+      float lse2[16], del[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = i0 + g * 8 + hl * 4 + e;
+          const float l = i < a.Nq ? lse_h[i] : -INFINITY;
+          lse2[g * 4 + e] = l > -INFINITY ? l * kLog2e : INFINITY;
+          del[g * 4 + e] = i < a.Nq ? del_h[i] : 0.f;
+        }
+      if (cls == 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = i0 + (r >> 2) * 8 + hl * 4 + (r & 3);
+          const bool ok = i < a.Nq && my_key < a.Nk && key_lo(ms, i) <= my_key && my_key <= key_hi(ms, i);
+          sc[r] = ok ? sc[r] : -INFINITY;
+        }
+      }
+      uint32_t pk[8], dsk[8];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c2, -lse2[r]));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r + 1], c2, -lse2[r + 1]));
+        pk[r >> 1] = TR::pack(p0, p1);
+        dsk[r >> 1] = TR::pack(p0 * (dp[r] - del[r]), p1 * (dp[r + 1] - del[r + 1]));
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS (k = the block's 32 queries, two halves of 16)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const i32x4 pop = i32x4{(int)pk[4 * half], (int)pk[4 * half + 1], (int)pk[4 * half + 2], (int)pk[4 * half + 3]};
+        const i32x4 dsop = i32x4{(int)dsk[4 * half], (int)dsk[4 * half + 1], (int)dsk[4 * half + 2], (int)dsk[4 * half + 3]};
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dv[db] = TR::mfma(tr_operand<D>(dring_a + s, toff, qb, half, db), pop, dv[db]);
+          dk[db] = TR::mfma(tr_operand<D>(qring_a + s, toff, qb, half, db), dsop, dk[db]);
+        }
+      }
+    }
+    barrier_keep(more ? 2 * CH : 0);
+  }
+
+  if (my_key >= a.Nk) return;
+  const uint32_t dk_rowb = (uint32_t)(a.dk_n * ES), dv_rowb = (uint32_t)(a.dv_n * ES);
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const uint32_t k0v = TR::pack(dk[db][4 * q4 + 0] * a.scale, dk[db][4 * q4 + 1] * a.scale);
+      const uint32_t k1v = TR::pack(dk[db][4 * q4 + 2] * a.scale, dk[db][4 * q4 + 3] * a.scale);
+      const uint32_t v0v = TR::pack(dv[db][4 * q4 + 0], dv[db][4 * q4 + 1]);
+      const uint32_t v1v = TR::pack(dv[db][4 * q4 + 2], dv[db][4 * q4 + 3]);
+      const uint32_t col = (db * 32 + q4 * 8 + hl * 4) * ES;
+      __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)k0v, (int)k1v}, dk_r, (uint32_t)my_key * dk_rowb + col, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)v0v, (int)v1v}, dv_r, (uint32_t)my_key * dv_rowb + col, 0, 0);
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+template <class TR, int D>
+static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Nq;
+  const int64_t delta_blocks = (rows * (D / 8) + 255) / 256;
+  hipLaunchKernelGGL((fa_bwd_delta_kernel<TR, D>), dim3((unsigned)delta_blocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<TR, D>), dim3((unsigned)((int64_t)a.B * a.Hkv * a.num_k_tiles)), dim3(256), 0,
+                     stream, a);
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<TR, D>), dim3((unsigned)((int64_t)a.B * a.Hq * a.num_q_tiles)), dim3(256), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int D, int dtype, hipStream_t stream) {
+  if (dtype == 0) return D == 64 ? launch_bwd_t<F16, 64>(a, stream) : launch_bwd_t<F16, 128>(a, stream);
+  return D == 64 ? launch_bwd_t<BF16, 64>(a, stream) : launch_bwd_t<BF16, 128>(a, stream);
+}
+
+}  // namespace fa

@@ -25,6 +25,33 @@ struct FwdArgs {
   float out_scale;       // 1, or dv for fp8
 };
 
+// Backward pass: one launch of each of three kernels (delta, dq, dk/dv).
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;          // [B, Hq, Nq] workspace: rowsum(dout * out)
+  int B, Nq, Nk, Hq, Hkv, group;
+  int causal, wl, wr;
+  int num_q_tiles;       // of the dq kernel's query tiles
+  int num_k_tiles;       // of the dk/dv kernel's key tiles
+  int64_t q_b, q_n, q_h, k_b, k_n, k_h, v_b, v_n, v_h, o_b, o_n, o_h;
+  int64_t do_b, do_n, do_h, dq_b, dq_n, dq_h, dk_b, dk_n, dk_h, dv_b, dv_n, dv_h;
+  uint32_t q_bytes, k_bytes, v_bytes, o_bytes, do_bytes, dq_bytes, dk_bytes, dv_bytes;
+  float scale;           // softmax_scale
+  float scale_log2;      // softmax_scale * log2(e)
+};
+
+constexpr int kBwdQRows = 128;   // query rows per dq workgroup
+constexpr int kBwdKRows = 128;   // keys per dk/dv workgroup
+hipError_t launch_bwd(const BwdArgs& a, int D, int dtype, hipStream_t stream);
+
 // Tile shapes of the launch for head dimension D and storage type.
 struct TileShape {
   int block_m, block_n, waves, lds_bytes;

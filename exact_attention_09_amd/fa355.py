@@ -20,12 +20,16 @@ _DTYPE_CODE = {torch.float16: FA_F16, torch.bfloat16: FA_BF16, torch.float8_e4m3
 _OUT_DTYPE = {FA_F16: torch.float16, FA_BF16: torch.bfloat16, FA_FP8_E4M3: torch.bfloat16}
 
 # Every symbol include/fa355.h declares.
-EXPORTED = ("fa_fwd", "fa_status_str", "fa_fwd_plan", "fa_kv_tile_range", "fa_version")
+EXPORTED = ("fa_fwd", "fa_bwd", "fa_status_str", "fa_fwd_plan", "fa_kv_tile_range", "fa_version")
 
 
 class FaStrides(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in
                 ("q_b", "q_n", "q_h", "k_b", "k_n", "k_h", "v_b", "v_n", "v_h", "o_b", "o_n", "o_h")]
+
+
+class FaBwdStrides(ctypes.Structure):
+    _fields_ = [(f"{t}_{a}", ctypes.c_int64) for t in ("q", "k", "v", "o", "do", "dq", "dk", "dv") for a in "bnh"]
 
 
 class FaPlanInfo(ctypes.Structure):
@@ -36,7 +40,7 @@ class FaPlanInfo(ctypes.Structure):
 
 class FaError(RuntimeError):
     def __init__(self, status: int, message: str):
-        super().__init__(f"fa_fwd failed: status {status}: {message}")
+        super().__init__(f"libfa355 call failed: status {status}: {message}")
         self.status = status
 
 
@@ -56,6 +60,9 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                            c_int, c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(FaStrides),
                            c_float, c_int, c_int, c_int, c_int, c_void_p, ctypes.POINTER(c_float)]
+    lib.fa_bwd.restype = c_int
+    lib.fa_bwd.argtypes = [c_void_p] * 10 + [c_int] * 6 + [ctypes.POINTER(FaBwdStrides), c_float, c_int, c_int, c_int,
+                                              c_int, c_void_p]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_status_str.argtypes = [c_int]
     lib.fa_fwd_plan.restype = c_int
@@ -148,3 +155,43 @@ def kv_tile_range(Nq, Nk, causal, window, block_n, row_begin, row_end):
     if st != 0:
         raise FaError(st, status_str(st))
     return tuple(x.value for x in vals)
+
+
+def bwd_raw(q, k, v, out, dout, lse, dq, dk, dv, delta, causal=False, window=(-1, -1), softmax_scale=None,
+            stream=None) -> int:
+    """Call fa_bwd on caller-provided tensors; returns the status code (0 = ok) without raising."""
+    lib = load()
+    code = _DTYPE_CODE.get(q.dtype)
+    if code is None:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    B, Nq, Hq, D = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    scale = float(D) ** -0.5 if softmax_scale is None else float(softmax_scale)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = FaBwdStrides()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", out), ("do", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.stride(3) != 1:
+            raise ValueError(f"{name}: the head dimension must be contiguous (stride 1), got {t.stride()}")
+        setattr(st, name + "_b", t.stride(0))
+        setattr(st, name + "_n", t.stride(1))
+        setattr(st, name + "_h", t.stride(2))
+    return lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, Nq, Nk, Hq, Hkv, D,
+                      ctypes.byref(st), scale, int(bool(causal)), int(window[0]), int(window[1]), code, stream)
+
+
+def bwd(q, k, v, out, dout, lse, causal=False, window=(-1, -1), softmax_scale=None):
+    """FlashAttention backward on the GPU: (dq, dk, dv) for the forward pass that produced
+    ``out`` and ``lse`` from q, k, v with the same options, given dout = dLoss/dout."""
+    if not all(t.is_cuda for t in (q, k, v, out, dout, lse)):
+        raise ValueError("all tensors must be device tensors")
+    B, Nq, Hq, D = q.shape
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    delta = torch.empty(B, Hq, Nq, dtype=torch.float32, device=q.device)
+    status = bwd_raw(q, k, v, out, dout, lse, dq, dk, dv, delta, causal, window, softmax_scale)
+    if status != 0:
+        raise FaError(status, status_str(status))
+    return dq, dk, dv

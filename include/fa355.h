@@ -1,5 +1,6 @@
 /*
- * fa355.h — C ABI of libfa355: the FlashAttention forward pass on AMD MI355X (gfx950).
+ * fa355.h — C ABI of libfa355: the FlashAttention forward pass (and its backward pass, fa_bwd)
+ * on AMD MI355X (gfx950).
  *
  * What is computed ("Flash Attention - Fast Memory-Efficient Attention", skill page, Workflow 1
  * Step 2 and Workflow 2 Steps 2-3; "What FlashAttention is and how it speeds up attention",
@@ -94,6 +95,47 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* out, float* 
                  int B, int Nq, int Nk, int Hq, int Hkv, int D, const fa_strides* strides,
                  float softmax_scale, int causal, int window_left, int window_right,
                  fa_dtype dtype, hipStream_t stream, const float* descale_qkv);
+
+/* Element strides of the backward pass's tensors (headdim stride 1). */
+typedef struct fa_bwd_strides {
+  int64_t q_b, q_n, q_h;
+  int64_t k_b, k_n, k_h;
+  int64_t v_b, v_n, v_h;
+  int64_t o_b, o_n, o_h;        /* out of the forward pass                         */
+  int64_t do_b, do_n, do_h;     /* dout: gradient of the loss w.r.t. out            */
+  int64_t dq_b, dq_n, dq_h;
+  int64_t dk_b, dk_n, dk_h;
+  int64_t dv_b, dv_n, dv_h;
+} fa_bwd_strides;
+
+/*
+ * fa_bwd — enqueue the backward pass of fa_fwd on `stream`: the gradients of a loss with respect
+ * to q, k and v, given dout, the gradient of the loss with respect to out. The pages name the
+ * backward pass and its recomputation of attention from the saved statistics ("Flash Attention -
+ * Fast Memory-Efficient Attention", skill page, Quick start; "What FlashAttention is and how it
+ * speeds up attention", section "Versions, hardware and sources"); with p_ij the softmax weights
+ * of the forward pass (recomputed from q, k and lse),
+ *   dv_j = sum_i p_ij dout_i,   ds_ij = p_ij (dout_i . v_j - dout_i . out_i),
+ *   dq_i = softmax_scale * sum_j ds_ij k_j,   dk_j = softmax_scale * sum_i ds_ij q_i,
+ * summed over the query heads that share a K/V head (MQA/GQA).
+ *
+ * q, k, v, out, lse  device: the forward pass's inputs and outputs for the same sizes, options
+ *                    and dtype (lse is required here: fp32 [B, Hq, Nq], contiguous).
+ * dout               device, [B, Nq, Hq, D], dtype storage.
+ * dq                 device, [B, Nq, Hq, D];  dk, dv: device, [B, Nk, Hkv, D]; dtype storage.
+ *                    Written in full (every row, including rows with no admitted key: zero).
+ *                    Must not alias each other or the inputs.
+ * delta              device fp32 [B, Hq, Nq] contiguous workspace (rowsum(dout * out)); the
+ *                    caller allocates it; its contents on entry do not matter.
+ * dtype              FA_F16 or FA_BF16 (FA_FP8_E4M3 returns FA_ERR_DTYPE).
+ * Other arguments, validation, ownership and asynchrony as for fa_fwd. Deterministic: no
+ * atomics; the same inputs give bitwise the same gradients.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, float* delta,
+                 int B, int Nq, int Nk, int Hq, int Hkv, int D, const fa_bwd_strides* strides,
+                 float softmax_scale, int causal, int window_left, int window_right,
+                 fa_dtype dtype, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_str(fa_status s);
