@@ -10,6 +10,10 @@ Metric: attention forward TFLOP/s with FLOPs = 4 * B * Hq * Nq * Nk * D, halved 
 a sliding window the admitted-pair count replaces Nq * Nk (4 * B * Hq * D * pairs). Inputs are
 resident in device memory before the timed region. Prints one JSON line.
 
+``--pass bwd`` times the backward pass (fa_bwd: dq, dk, dv for a seeded N(0, 1) upstream gradient,
+after one forward pass that provides out and lse) on the same workload; its FLOPs are counted as
+2.5 times the forward's (the five products of the method's backward pass).
+
 Also reported:
   * roofline — the kernel's achieved TFLOP/s against MI355X's dense MFMA peak for its dtype,
     from HIP events recorded around each launch on the launch stream (mean and median per
@@ -35,6 +39,8 @@ PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "e4m3": 5033.2}   # 256 CU x 2.4 G
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "causal_b4_h32_n4096_d64_f16"
 METRIC = "attention fwd TFLOP/s (4·B·H·Nq·Nk·D, causal halved) and % of MFMA peak"
+METRIC_BWD = "attention bwd TFLOP/s (2.5 x the forward FLOPs: five products of the forward's size)"
+BWD_FLOP_FACTOR = 2.5
 KERNEL_SOURCES = ["exact_attention_09_amd/csrc/fa_fwd_f16.hip", "exact_attention_09_amd/csrc/fa_f16_common.hpp",
                   "exact_attention_09_amd/csrc/fa_fwd_fp8.hip", "exact_attention_09_amd/csrc/fa_device.hpp",
                   "exact_attention_09_amd/csrc/fa_mask.hpp", "exact_attention_09_amd/csrc/fa_kernels.hpp",
@@ -69,6 +75,14 @@ def algorithmic_bytes(w):
             + w.B * w.Hq * w.Nq * 4)
 
 
+def algorithmic_bytes_bwd(w):
+    """Bytes the backward pass must move at least: q, k, v, out, dout, lse read once; dq, dk, dv
+    written once; the delta row sums written and read once."""
+    es = 2
+    rows_q = w.B * w.Nq * w.Hq
+    return (4 * rows_q * w.D * es + 4 * w.B * w.Nk * w.Hkv * w.D * es + rows_q * 4 + 2 * rows_q * 4)
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -89,11 +103,12 @@ def committed_traffic(workload):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, q, k, v, descale, budget_s):
-    """Time the fp64 oracle on whole heads of the same inputs until budget_s has passed."""
+def cpu_baseline(w, q, k, v, descale, budget_s, dout=None):
+    """Time the fp64 oracle on whole heads of the same inputs until budget_s has passed (the
+    gradient oracle when dout is given)."""
     import numpy as np
 
-    from oracle import attention_fp64, decode_bf16_bits, decode_e4m3_codes, decode_f16_bits
+    from oracle import attention_bwd_fp64, attention_fp64, decode_bf16_bits, decode_e4m3_codes, decode_f16_bits
 
     def dec(x, s):
         import torch
@@ -122,20 +137,24 @@ def cpu_baseline(w, q, k, v, descale, budget_s):
             qh = dec(q[b:b + 1, :, h:h + 1, :], dq)
             kh = dec(k[b:b + 1, :, g:g + 1, :], dk)
             vh = dec(v[b:b + 1, :, g:g + 1, :], dv)
-            attention_fp64(qh, kh, vh, w.softmax_scale(), w.causal, w.window)
+            if dout is None:
+                attention_fp64(qh, kh, vh, w.softmax_scale(), w.causal, w.window)
+            else:
+                attention_bwd_fp64(qh, kh, vh, dec(dout[b:b + 1, :, h:h + 1, :], 1.0), w.softmax_scale(), w.causal,
+                                   w.window)
             heads += 1
             elapsed = time.perf_counter() - t0
             if elapsed >= budget_s:
                 break
         if elapsed >= budget_s:
             break
-    per_head_flops = metric_flops(w) / (w.B * w.Hq)
+    per_head_flops = metric_flops(w) * (1.0 if dout is None else BWD_FLOP_FACTOR) / (w.B * w.Hq)
     return {
         "value": heads * per_head_flops / elapsed / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{heads} of {w.B * w.Hq} (batch, head) pairs of the same inputs, full fp64 score matrix per "
+        "sample": f"{heads} of {w.B * w.Hq} (batch, head) pairs of the same inputs{' (gradients)' if dout is not None else ''}, full fp64 score matrix per "
                   f"head, {elapsed:.1f} s wall; metric FLOPs of those heads / wall time; BLAS={blas_name} "
                   f"threads={threads}, host logical CPUs={os.cpu_count()}",
     }
@@ -147,6 +166,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward pass (default, the headline metric) or the backward pass")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                     help="oracle time budget on the host; 0 skips the CPU baseline")
     ap.add_argument("--cold-launches", type=int, default=10,
@@ -192,11 +213,30 @@ def main():
                       device=dev)
     lse = torch.empty(w.B, w.Hq, w.Nq, dtype=torch.float32, device=dev)
     scale = w.softmax_scale()
+    bwd = args.pass_ == "bwd"
+    if bwd and w.dtype == "e4m3":
+        print(json.dumps({"error": "the backward pass takes fp16 or bf16 inputs"}))
+        sys.exit(2)
 
-    def step():
+    def fwd_step():
         st = fa.fwd_raw(qd, kd, vd, out, lse, w.causal, w.window, scale, descale)
         if st != 0:
             raise fa.FaError(st, fa.status_str(st))
+
+    step = fwd_step
+    if bwd:
+        # upstream gradient: seeded N(0, 1) in the storage type; out and lse from one forward pass
+        g = torch.Generator().manual_seed(seed + 1)
+        dout = torch.randn(w.B, w.Nq, w.Hq, w.D, generator=g).to(q.dtype)
+        dod = dout.to(dev)
+        fwd_step()
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+        delta = torch.empty(w.B, w.Hq, w.Nq, dtype=torch.float32, device=dev)
+
+        def step():
+            st = fa.bwd_raw(qd, kd, vd, out, dod, lse, dq, dk, dv, delta, w.causal, w.window, scale)
+            if st != 0:
+                raise fa.FaError(st, fa.status_str(st))
 
     for _ in range(args.warmup):
         step()
@@ -234,16 +274,17 @@ def main():
         del flush
         cold_med = sorted(cold_ms)[len(cold_ms) // 2] / 1e3
         cold = {"launches": args.cold_launches, "kernel_median_us": round(cold_med * 1e6, 3),
-                "TFLOPs": round(metric_flops(w) / cold_med / 1e12, 2)}
+                "TFLOPs": round(metric_flops(w) * (BWD_FLOP_FACTOR if bwd else 1.0) / cold_med / 1e12, 2)}
 
-    flops = metric_flops(w)
+    flops = metric_flops(w) * (BWD_FLOP_FACTOR if bwd else 1.0)
     value = flops / (ms_per_step / 1e3) / 1e12
     achieved = flops / avg_kernel_s / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = committed_traffic(w.name)
+    traffic = committed_traffic(("bwd_" if bwd else "") + w.name)
+    alg_bytes = algorithmic_bytes_bwd(w) if bwd else algorithmic_bytes(w)
 
     rec = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if bwd else METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -263,13 +304,16 @@ def main():
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel_avg_us": round(avg_kernel_s * 1e6, 3),
                      "kernel_median_us": round(med_kernel_s * 1e6, 3),
-                     "algorithmic_bytes": algorithmic_bytes(w),
-                     "algorithmic_GBps": round(algorithmic_bytes(w) / avg_kernel_s / 1e9, 1)},
+                     "algorithmic_bytes": alg_bytes,
+                     "algorithmic_GBps": round(alg_bytes / avg_kernel_s / 1e9, 1)},
     }
     if cold is not None:
         rec["cold_cache"] = cold
+    if bwd:
+        rec["config"]["pass"] = "bwd"
     if args.cpu_baseline_seconds > 0:
-        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, descale, args.cpu_baseline_seconds)
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, descale, args.cpu_baseline_seconds,
+                                           dout if bwd else None)
     print(json.dumps(rec), flush=True)
 
 

@@ -287,6 +287,9 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[4 * TILEB];   // [Q0 Q1 | dO0 dO1]
   char* const qring = smem;
   char* const dring = smem + 2 * TILEB;
+  // lse and delta of each slot's 64 query rows (1 KB per row set: the 4-byte LDS-direct load of a
+  // wave covers 256 bytes, the rest is slack)
+  __shared__ __attribute__((aligned(16))) char sbuf[2 * 2 * 1024];
 
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -354,22 +357,36 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) dma16(d, goff[i], soff, lds + wave * 64 * 16 + i * NT * 16);
   };
-  auto barrier_keep = [&](int pending) {
+  // waits for this thread's loads older than the newest step's (2 CH + 2 of them), then meets
+  // the other waves
+  constexpr int PEND = 2 * CH + 2;
+  static_assert(PEND < 16, "vmcnt immediate below");
+  auto barrier_keep = [&](bool keep_newest) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (pending >= 2 * CH) __builtin_amdgcn_s_waitcnt(0x0070 | (2 * CH));
+    if (keep_newest) __builtin_amdgcn_s_waitcnt(0x0070 | PEND);
     else __builtin_amdgcn_s_waitcnt(0x0070);
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
+
   // step n -> (query head h, query tile u)
   auto head_of = [&](int n) { return hk * a.group + n / nu; };
   auto tile_of = [&](int n) { return ub + n % nu; };
+  const uint32_t sbuf_a = lds_addr_of(sbuf);
+  // loads of step n into ring slot `slot` (0 or TILEB): Q and dO tiles, and the tile's lse and
+  // delta (every wave loads those 64 values into the same place: 2 loads, same count per wave)
   auto issue = [&](int n, uint32_t slot) {
     const int hh = head_of(n), u = tile_of(n);
     const BufDesc q_d = make_desc((const char*)a.q + (b * a.q_b + hh * a.q_h) * ES, a.q_bytes);
     const BufDesc d_d = make_desc((const char*)a.dout + (b * a.do_b + hh * a.do_h) * ES, a.do_bytes);
     dma(q_d, qgoff, (uint32_t)(u * BQ) * q_rowb, qring_a + slot);
     dma(d_d, dgoff, (uint32_t)(u * BQ) * do_rowb, dring_a + slot);
+    const int64_t row0 = ((int64_t)b * a.Hq + hh) * a.Nq;
+    const BufDesc l_d = make_desc(a.lse + row0, (uint32_t)a.Nq * 4u);
+    const BufDesc e_d = make_desc(a.delta + row0, (uint32_t)a.Nq * 4u);
+    const uint32_t st = sbuf_a + (slot ? 2048u : 0u);
+    dma4(l_d, lane * 4, (uint32_t)(u * BQ) * 4u, st);
+    dma4(e_d, lane * 4, (uint32_t)(u * BQ) * 4u, st + 1024);
   };
   int roff[KS];
 #pragma unroll
@@ -386,7 +403,7 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
     const int64_t j1 = min(kw0 + 31, a.Nk - 1);
     if (kw0 >= a.Nk || i0 >= a.Nq) return 0;
     if (key_hi(ms, i1) < kw0 || key_lo(ms, i0) > j1) return 0;
-    if (key_lo(ms, i1) <= kw0 && kw0 + 31 <= key_hi(ms, i0)) return 2;
+    if (i0 + 31 < a.Nq && key_lo(ms, i1) <= kw0 && kw0 + 31 <= key_hi(ms, i0)) return 2;
     return 1;
   };
 
@@ -400,10 +417,9 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
     const uint32_t s = (uint32_t)(n & 1) * TILEB;
     const bool more = n + 1 < nsteps;
     if (more) issue(n + 1, TILEB - s);
-    barrier_keep(more ? 2 * CH : 0);
-    const int hh = head_of(n), u = tile_of(n);
-    const float* lse_h = a.lse + ((int64_t)b * a.Hq + hh) * a.Nq;
-    const float* del_h = a.delta + ((int64_t)b * a.Hq + hh) * a.Nq;
+    barrier_keep(more);
+    const int u = tile_of(n);
+    const uint32_t st = sbuf_a + (s ? 2048u : 0u);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int i0 = u * BQ + qb * 32;
@@ -416,17 +432,19 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
         sc = TR::mfma(lds_read_b128(opaque_vbase(qring_a + s + roff[ks]) + qb * 32 * ROWB), kop[ks], sc);
         dp = TR::mfma(lds_read_b128(opaque_vbase(dring_a + s + roff[ks]) + qb * 32 * ROWB), vop[ks], dp);
       }
-      // accumulator r holds query i0 + (r/4)*8 + hl*4 + r%4
+      // accumulator r holds query i0 + (r/4)*8 + hl*4 + r%4: four groups of four consecutive rows
       float lse2[16], del[16];
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t at = st + (uint32_t)(qb * 32 + g * 8 + hl * 4) * 4u;
+        const i32x4 lv = lds_read_b128(at), dv4 = lds_read_b128(at + 1024);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int i = i0 + g * 8 + hl * 4 + e;
-          const float l = i < a.Nq ? lse_h[i] : -INFINITY;
-          lse2[g * 4 + e] = l > -INFINITY ? l * kLog2e : INFINITY;
-          del[g * 4 + e] = i < a.Nq ? del_h[i] : 0.f;
+          const float l = __int_as_float(lv[e]);
+          lse2[g * 4 + e] = l > -INFINITY ? l * kLog2e : INFINITY;   // no admitted key: p = 0
+          del[g * 4 + e] = __int_as_float(dv4[e]);
         }
+      }
       if (cls == 1) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -455,7 +473,7 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
         }
       }
     }
-    barrier_keep(more ? 2 * CH : 0);
+    barrier_keep(more);
   }
 
   if (my_key >= a.Nk) return;

@@ -99,6 +99,21 @@ __device__ inline void dma16(const BufDesc& d, uint32_t voff, uint32_t soff, uin
       : "v"(voff), "s"(rs), "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "s"(__builtin_amdgcn_readfirstlane(soff))
       : "memory");
 }
+// The 4-byte form: lane l's 4 bytes land at LDS byte address lds_addr + 4 * l.
+__device__ inline void dma4(const BufDesc& d, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 rs = u32x4{d.w[0], d.w[1], d.w[2], d.w[3]};
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %1, %2, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(rs), "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "s"(__builtin_amdgcn_readfirstlane(soff))
+      : "memory");
+}
 // LDS reads addressed by 32-bit LDS byte addresses. Going through an integer address (instead of a
 // generic pointer) lets the compiler put constant displacements into the instruction's offset field
 // instead of recomputing each address with vector adds.
