@@ -77,10 +77,10 @@ def algorithmic_bytes(w):
 
 def algorithmic_bytes_bwd(w):
     """Bytes the backward pass must move at least: q, k, v, out, dout, lse read once; dq, dk, dv
-    written once; the delta row sums written and read once."""
+    written once; the workspace (row sums dout . out and lse in base 2) written and read once."""
     es = 2
     rows_q = w.B * w.Nq * w.Hq
-    return (4 * rows_q * w.D * es + 4 * w.B * w.Nk * w.Hkv * w.D * es + rows_q * 4 + 2 * rows_q * 4)
+    return (4 * rows_q * w.D * es + 4 * w.B * w.Nk * w.Hkv * w.D * es + rows_q * 4 + 4 * rows_q * 4)
 
 
 def kernel_source_hash():
@@ -231,10 +231,10 @@ def main():
         dod = dout.to(dev)
         fwd_step()
         dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
-        delta = torch.empty(w.B, w.Hq, w.Nq, dtype=torch.float32, device=dev)
+        ws = fa.bwd_workspace(qd)
 
         def step():
-            st = fa.bwd_raw(qd, kd, vd, out, dod, lse, dq, dk, dv, delta, w.causal, w.window, scale)
+            st = fa.bwd_raw(qd, kd, vd, out, dod, lse, dq, dk, dv, ws, w.causal, w.window, scale)
             if st != 0:
                 raise fa.FaError(st, fa.status_str(st))
 

@@ -197,10 +197,10 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* out, float* 
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
-                 void* dq, void* dk, void* dv, float* delta, int B, int Nq, int Nk, int Hq, int Hkv, int D,
+                 void* dq, void* dk, void* dv, float* workspace, int B, int Nq, int Nk, int Hq, int Hkv, int D,
                  const fa_bwd_strides* s, float softmax_scale, int causal, int window_left, int window_right,
                  fa_dtype dtype, hipStream_t stream) {
-  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !delta || !s) return FA_ERR_NULL;
+  if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !workspace || !s) return FA_ERR_NULL;
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   fa_status st = check_sizes(B, Nq, Nk, Hq, Hkv, D, window_left, window_right, dtype);
   if (st != FA_OK) return st;
@@ -218,12 +218,12 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* out, c
   const void* ptrs[9] = {q, k, v, out, dout, dq, dk, dv, nullptr};
   for (int i = 0; i < 8; ++i)
     if (!aligned16(ptrs[i])) return FA_ERR_STRIDES;
-  if (((uintptr_t)lse & 3u) || ((uintptr_t)delta & 3u)) return FA_ERR_STRIDES;
+  if (((uintptr_t)lse & 3u) || ((uintptr_t)workspace & 3u)) return FA_ERR_STRIDES;
   if ((int64_t)B * Hq * Nq >= ((int64_t)1 << 31) / 16) return FA_ERR_SHAPE;
 
   fa::BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = out; a.dout = dout; a.lse = lse;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.delta = delta;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.delta = workspace;
   a.B = B; a.Nq = Nq; a.Nk = Nk; a.Hq = Hq; a.Hkv = Hkv; a.group = Hq / Hkv;
   a.causal = causal ? 1 : 0;
   a.wl = window_left;

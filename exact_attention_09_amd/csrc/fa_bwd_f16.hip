@@ -47,7 +47,9 @@ __device__ inline void unpack2(uint32_t w, float& x, float& y) {
 constexpr float kLog2e = 1.44269504088896340736f;
 
 // ---------------------------------------------------------------------------------------------
-// delta[b, h, i] = sum_d dout[b, i, h, d] * out[b, i, h, d]; D/8 lanes per row, 16 bytes each.
+// Per query row r = (b, h, i): delta[r] = sum_d dout[b, i, h, d] * out[b, i, h, d], and in the
+// second half of the workspace lse[r] * log2(e) (+inf for a row with no admitted key, so that its
+// p = 2^(s - lse2) is 0). D/8 lanes per row, 16 bytes each.
 template <class TR, int D>
 __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(BwdArgs a) {
   constexpr int LPR = D / 8;
@@ -72,7 +74,11 @@ __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  if (row < nrows && part == 0) a.delta[row] = s;
+  if (row < nrows && part == 0) {
+    a.delta[row] = s;
+    const float l = a.lse[row];
+    a.delta[nrows + row] = l > -INFINITY ? l * kLog2e : INFINITY;
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -102,13 +108,22 @@ struct BwdTile {
 // rows kb*32 + half*16 + (t / 4) * 8 + (l / 32) * 4 + t % 4 for k-slot (l / 32) * 8 + t, i.e. the
 // order in which a 32x32 accumulator holds its rows, so that an accumulator packed to 16 bits is
 // the matching B operand.
+// `base` holds the slot's address plus the lane's two offsets (tr_bases), so that the block and
+// half land in the reads' immediate offsets.
 template <int D>
-__device__ inline i32x4 tr_operand(uint32_t slot, const int (&toff)[D / 32][2], int kb, int half, int db) {
+__device__ inline i32x4 tr_operand(const uint32_t (&base)[D / 32][2], int kb, int half, int db) {
   constexpr int ROWB = D * 2;
-  const uint32_t p0 = opaque_vbase(slot + toff[db][0]) + (kb * 32 + half * 16) * ROWB;
-  const uint32_t p1 = opaque_vbase(slot + toff[db][1]) + (kb * 32 + half * 16 + 8) * ROWB;
-  const i32x2 v0 = lds_read_tr16(p0), v1 = lds_read_tr16(p1);
+  const i32x2 v0 = lds_read_tr16(base[db][0] + (kb * 32 + half * 16) * ROWB);
+  const i32x2 v1 = lds_read_tr16(base[db][1] + (kb * 32 + half * 16 + 8) * ROWB);
   return i32x4{v0[0], v0[1], v1[0], v1[1]};
+}
+
+template <int D>
+__device__ inline void tr_bases(uint32_t slot, const int (&toff)[D / 32][2], uint32_t (&base)[D / 32][2]) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int e8 = 0; e8 < 2; ++e8) base[db][e8] = opaque_vbase(slot + toff[db][e8]);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -217,6 +232,8 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(BwdArgs a) {
     barrier_keep(more ? 2 * CH : 0);   // tile t landed for every wave
     const bool live = wave_live && t * BN + BN - 1 >= wlo0 && t * BN <= whi1;
     if (live) {
+      uint32_t kt_base[DB][2];
+      tr_bases<D>(kring_a + s, toff, kt_base);
       f32x16 st[KB], dpt[KB];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) st[kb] = dpt[kb] = f32x16{};
@@ -258,7 +275,7 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(BwdArgs a) {
           const i32x4 dsop = i32x4{(int)dsk[kb][4 * half + 0], (int)dsk[kb][4 * half + 1], (int)dsk[kb][4 * half + 2],
                                    (int)dsk[kb][4 * half + 3]};
 #pragma unroll
-          for (int db = 0; db < DB; ++db) dq[db] = TR::mfma(tr_operand<D>(kring_a + s, toff, kb, half, db), dsop, dq[db]);
+          for (int db = 0; db < DB; ++db) dq[db] = TR::mfma(tr_operand<D>(kt_base, kb, half, db), dsop, dq[db]);
         }
     }
     barrier_keep(more ? 2 * CH : 0);   // every wave is done with slot s before it is refilled
@@ -287,7 +304,7 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[4 * TILEB];   // [Q0 Q1 | dO0 dO1]
   char* const qring = smem;
   char* const dring = smem + 2 * TILEB;
-  // lse and delta of each slot's 64 query rows (1 KB per row set: the 4-byte LDS-direct load of a
+  // base-2 lse and delta of each slot's 64 query rows (1 KB per row set: the 4-byte LDS-direct load of a
   // wave covers 256 bytes, the rest is slack)
   __shared__ __attribute__((aligned(16))) char sbuf[2 * 2 * 1024];
 
@@ -373,8 +390,8 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
   auto head_of = [&](int n) { return hk * a.group + n / nu; };
   auto tile_of = [&](int n) { return ub + n % nu; };
   const uint32_t sbuf_a = lds_addr_of(sbuf);
-  // loads of step n into ring slot `slot` (0 or TILEB): Q and dO tiles, and the tile's lse and
-  // delta (every wave loads those 64 values into the same place: 2 loads, same count per wave)
+  // loads of step n into ring slot `slot` (0 or TILEB): Q and dO tiles, and the tile's base-2 lse
+  // and delta (every wave loads those 64 values into the same place: 2 loads, same count per wave)
   auto issue = [&](int n, uint32_t slot) {
     const int hh = head_of(n), u = tile_of(n);
     const BufDesc q_d = make_desc((const char*)a.q + (b * a.q_b + hh * a.q_h) * ES, a.q_bytes);
@@ -382,7 +399,7 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
     dma(q_d, qgoff, (uint32_t)(u * BQ) * q_rowb, qring_a + slot);
     dma(d_d, dgoff, (uint32_t)(u * BQ) * do_rowb, dring_a + slot);
     const int64_t row0 = ((int64_t)b * a.Hq + hh) * a.Nq;
-    const BufDesc l_d = make_desc(a.lse + row0, (uint32_t)a.Nq * 4u);
+    const BufDesc l_d = make_desc(a.delta + (int64_t)a.B * a.Hq * a.Nq + row0, (uint32_t)a.Nq * 4u);
     const BufDesc e_d = make_desc(a.delta + row0, (uint32_t)a.Nq * 4u);
     const uint32_t st = sbuf_a + (slot ? 2048u : 0u);
     dma4(l_d, lane * 4, (uint32_t)(u * BQ) * 4u, st);
@@ -420,6 +437,9 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
     barrier_keep(more);
     const int u = tile_of(n);
     const uint32_t st = sbuf_a + (s ? 2048u : 0u);
+    uint32_t qt_base[DB][2], dt_base[DB][2];
+    tr_bases<D>(qring_a + s, toff, qt_base);
+    tr_bases<D>(dring_a + s, toff, dt_base);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int i0 = u * BQ + qb * 32;
@@ -440,8 +460,7 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
         const i32x4 lv = lds_read_b128(at), dv4 = lds_read_b128(at + 1024);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float l = __int_as_float(lv[e]);
-          lse2[g * 4 + e] = l > -INFINITY ? l * kLog2e : INFINITY;   // no admitted key: p = 0
+          lse2[g * 4 + e] = __int_as_float(lv[e]);
           del[g * 4 + e] = __int_as_float(dv4[e]);
         }
       }
@@ -468,8 +487,8 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
         const i32x4 dsop = i32x4{(int)dsk[4 * half], (int)dsk[4 * half + 1], (int)dsk[4 * half + 2], (int)dsk[4 * half + 3]};
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          dv[db] = TR::mfma(tr_operand<D>(dring_a + s, toff, qb, half, db), pop, dv[db]);
-          dk[db] = TR::mfma(tr_operand<D>(qring_a + s, toff, qb, half, db), dsop, dk[db]);
+          dv[db] = TR::mfma(tr_operand<D>(dt_base, qb, half, db), pop, dv[db]);
+          dk[db] = TR::mfma(tr_operand<D>(qt_base, qb, half, db), dsop, dk[db]);
         }
       }
     }

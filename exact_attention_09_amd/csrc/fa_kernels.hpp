@@ -36,7 +36,8 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;          // [B, Hq, Nq] workspace: rowsum(dout * out)
+  float* delta;          // [2, B, Hq, Nq] workspace: rowsum(dout * out), then lse * log2(e)
+                         // (+inf for rows with no admitted key)
   int B, Nq, Nk, Hq, Hkv, group;
   int causal, wl, wr;
   int num_q_tiles;       // of the dq kernel's query tiles

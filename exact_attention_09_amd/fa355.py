@@ -157,9 +157,10 @@ def kv_tile_range(Nq, Nk, causal, window, block_n, row_begin, row_end):
     return tuple(x.value for x in vals)
 
 
-def bwd_raw(q, k, v, out, dout, lse, dq, dk, dv, delta, causal=False, window=(-1, -1), softmax_scale=None,
+def bwd_raw(q, k, v, out, dout, lse, dq, dk, dv, workspace, causal=False, window=(-1, -1), softmax_scale=None,
             stream=None) -> int:
-    """Call fa_bwd on caller-provided tensors; returns the status code (0 = ok) without raising."""
+    """Call fa_bwd on caller-provided tensors; returns the status code (0 = ok) without raising.
+    ``workspace``: fp32 device tensor of 2 * B * Hq * Nq elements (see ``bwd_workspace``)."""
     lib = load()
     code = _DTYPE_CODE.get(q.dtype)
     if code is None:
@@ -177,8 +178,14 @@ def bwd_raw(q, k, v, out, dout, lse, dq, dk, dv, delta, causal=False, window=(-1
         setattr(st, name + "_n", t.stride(1))
         setattr(st, name + "_h", t.stride(2))
     return lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, Nq, Nk, Hq, Hkv, D,
+                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, Nq, Nk, Hq, Hkv, D,
                       ctypes.byref(st), scale, int(bool(causal)), int(window[0]), int(window[1]), code, stream)
+
+
+def bwd_workspace(q):
+    """The fp32 workspace fa_bwd needs for queries q [B, Nq, Hq, D]: 2 * B * Hq * Nq floats."""
+    B, Nq, Hq, _ = q.shape
+    return torch.empty(2, B, Hq, Nq, dtype=torch.float32, device=q.device)
 
 
 def bwd(q, k, v, out, dout, lse, causal=False, window=(-1, -1), softmax_scale=None):
@@ -190,8 +197,7 @@ def bwd(q, k, v, out, dout, lse, causal=False, window=(-1, -1), softmax_scale=No
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    delta = torch.empty(B, Hq, Nq, dtype=torch.float32, device=q.device)
-    status = bwd_raw(q, k, v, out, dout, lse, dq, dk, dv, delta, causal, window, softmax_scale)
+    status = bwd_raw(q, k, v, out, dout, lse, dq, dk, dv, bwd_workspace(q), causal, window, softmax_scale)
     if status != 0:
         raise FaError(status, status_str(status))
     return dq, dk, dv

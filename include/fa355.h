@@ -125,14 +125,16 @@ typedef struct fa_bwd_strides {
  * dq                 device, [B, Nq, Hq, D];  dk, dv: device, [B, Nk, Hkv, D]; dtype storage.
  *                    Written in full (every row, including rows with no admitted key: zero).
  *                    Must not alias each other or the inputs.
- * delta              device fp32 [B, Hq, Nq] contiguous workspace (rowsum(dout * out)); the
- *                    caller allocates it; its contents on entry do not matter.
+ * workspace          device fp32 workspace of 2 * B * Hq * Nq floats, 4-byte aligned: the pass
+ *                    writes rowsum(dout * out) per query row into the first half and lse * log2(e)
+ *                    into the second, then reads them back. The caller allocates it; its contents
+ *                    on entry do not matter.
  * dtype              FA_F16 or FA_BF16 (FA_FP8_E4M3 returns FA_ERR_DTYPE).
  * Other arguments, validation, ownership and asynchrony as for fa_fwd. Deterministic: no
  * atomics; the same inputs give bitwise the same gradients.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                 const float* lse, void* dq, void* dk, void* dv, float* delta,
+                 const float* lse, void* dq, void* dk, void* dv, float* workspace,
                  int B, int Nq, int Nk, int Hq, int Hkv, int D, const fa_bwd_strides* strides,
                  float softmax_scale, int causal, int window_left, int window_right,
                  fa_dtype dtype, hipStream_t stream);

@@ -65,7 +65,7 @@ def test_bwd_rejects_bad_strides_and_alignment(lib):
         assert call(lib, strides=bad) == 6
     for i in range(10):
         if i in (5, 9):
-            continue                            # lse and delta need only 4-byte alignment
+            continue                            # lse and the workspace need only 4-byte alignment
         p = [P] * 10
         p[i] = P + 8                            # the 16-bit tensors need 16 bytes
         assert call(lib, ptrs=p) == 6
