@@ -83,16 +83,27 @@ __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------------------------
 // Shared pieces of the two tile kernels: the LDS tile layout (row-major, 16-byte chunks XOR-ed by
-// k_swz of the row) and the per-lane offsets of its row reads and transpose reads.
+// swz of the row) and the per-lane offsets of its row reads and transpose reads.
 template <int D>
 struct BwdTile {
   static constexpr int ROWB = D * 2;
   static constexpr int TILEB = 64 * ROWB;     // 64 rows
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
+  // Chunk swizzle, free of bank conflicts (64 banks of 4 bytes) for both kinds of read:
+  //  * a row read serves 16 lanes = 16 consecutive rows at one logical chunk per cycle; rows that
+  //    start on the same bank (every second row for 128-byte rows, every row for 256-byte rows)
+  //    must see distinct values of swz;
+  //  * a transpose read serves 32 lanes = 4 consecutive rows (4-aligned) x one aligned group of 4
+  //    chunks; rows that start on the same bank must differ in bit 2 (and 3) of swz, which moves
+  //    them to another group of 4 chunks.
+  // swz is unchanged by adding 16 rows and changed by adding 8.
+  __device__ static int swz(int r) {
+    return ROWB == 128 ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3)) : (((r & 3) << 2) | ((r >> 2) & 3));
+  }
   // Row read (A or B operand with the head dimension as k): row r (0..31 of a 32-row block),
   // k-slots ks*16 + hl*8 .. +7.
-  __device__ static int row_off(int r, int ks, int hl) { return r * ROWB + (((2 * ks + hl) ^ k_swz<ROWB>(r)) << 4); }
+  __device__ static int row_off(int r, int ks, int hl) { return r * ROWB + (((2 * ks + hl) ^ swz(r)) << 4); }
   // Transpose read (A operand with the rows as k): for 16-lane group g16 and lane s16 = 4 tr + tc,
   // rows 4 (g16 >> 1) + tr (+ 8 e8), columns db*32 + (g16 & 1)*16 + 4 tc .. +3. Adding 16 or 32
   // rows keeps the swizzle, adding 8 changes it, so each column block has two offsets.
@@ -100,7 +111,7 @@ struct BwdTile {
     const int g16 = lane >> 4, s16 = lane & 15, tr = s16 >> 2, tc = s16 & 3;
     const int row = 4 * (g16 >> 1) + tr;
     const int chunk = db * 4 + (g16 & 1) * 2 + (tc >> 1);
-    return row * ROWB + ((chunk ^ k_swz<ROWB>(row + 8 * e8)) << 4) + (tc & 1) * 8;
+    return row * ROWB + ((chunk ^ swz(row + 8 * e8)) << 4) + (tc & 1) * 8;
   }
 };
 
@@ -188,8 +199,8 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int pos = (i * NT + tid) * 16, row = pos / ROWB, pc = (pos % ROWB) / 16;
-    kgoff[i] = (uint32_t)row * k_rowb + ((pc ^ k_swz<ROWB>(row)) << 4);
-    vgoff[i] = (uint32_t)row * v_rowb + ((pc ^ k_swz<ROWB>(row)) << 4);
+    kgoff[i] = (uint32_t)row * k_rowb + ((pc ^ T::swz(row)) << 4);
+    vgoff[i] = (uint32_t)row * v_rowb + ((pc ^ T::swz(row)) << 4);
   }
   const BufDesc k_d = make_desc(kbp, a.k_bytes), v_d = make_desc(vbp, a.v_bytes);
   const uint32_t kring_a = lds_addr_of(kring), vring_a = lds_addr_of(vring);
@@ -366,8 +377,8 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
     const int pos = (i * NT + tid) * 16, row = pos / ROWB, pc = (pos % ROWB) / 16;
-    qgoff[i] = (uint32_t)row * q_rowb + ((pc ^ k_swz<ROWB>(row)) << 4);
-    dgoff[i] = (uint32_t)row * do_rowb + ((pc ^ k_swz<ROWB>(row)) << 4);
+    qgoff[i] = (uint32_t)row * q_rowb + ((pc ^ T::swz(row)) << 4);
+    dgoff[i] = (uint32_t)row * do_rowb + ((pc ^ T::swz(row)) << 4);
   }
   const uint32_t qring_a = lds_addr_of(qring), dring_a = lds_addr_of(dring);
   auto dma = [&](const BufDesc& d, const uint32_t* goff, uint32_t soff, uint32_t lds) {
@@ -386,14 +397,18 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
 
-  // step n -> (query head h, query tile u)
-  auto head_of = [&](int n) { return hk * a.group + n / nu; };
-  auto tile_of = [&](int n) { return ub + n % nu; };
+  // Steps run over the group's query heads (outer) and the query tiles ub .. ue - 1 (inner).
+  auto advance = [&](int& hh, int& u) {
+    if (++u == ue) {
+      u = ub;
+      ++hh;
+    }
+  };
   const uint32_t sbuf_a = lds_addr_of(sbuf);
-  // loads of step n into ring slot `slot` (0 or TILEB): Q and dO tiles, and the tile's base-2 lse
-  // and delta (every wave loads those 64 values into the same place: 2 loads, same count per wave)
-  auto issue = [&](int n, uint32_t slot) {
-    const int hh = head_of(n), u = tile_of(n);
+  // loads of the step (query head hh, query tile u) into ring slot `slot` (0 or TILEB): Q and dO
+  // tiles, and the tile's base-2 lse and delta (every wave loads those 64 values into the same
+  // place: 2 loads, same count per wave)
+  auto issue = [&](int hh, int u, uint32_t slot) {
     const BufDesc q_d = make_desc((const char*)a.q + (b * a.q_b + hh * a.q_h) * ES, a.q_bytes);
     const BufDesc d_d = make_desc((const char*)a.dout + (b * a.do_b + hh * a.do_h) * ES, a.do_bytes);
     dma(q_d, qgoff, (uint32_t)(u * BQ) * q_rowb, qring_a + slot);
@@ -414,13 +429,34 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int e8 = 0; e8 < 2; ++e8) toff[db][e8] = T::tr_off(lane, db, e8);
 
-  // this wave's keys against a 32-query block starting at row i0: all admitted, none, or some
+  // Query rows that admit some key of this wave, [sw_lo, sw_hi], and rows that admit all 32 of
+  // its keys, [aw_lo, aw_hi] (empty when the wave's keys run past Nk). With off = Nk - Nq and
+  // right = 0 under the causal mask (else window_right), row i admits key j iff
+  // i >= j - off - right (no bound when right < 0) and i <= j - off + window_left (no bound when
+  // window_left < 0); both bounds move by one row per key, so the rows that admit some key of
+  // j0..j1 run from the lower bound of j0 to the upper bound of j1, and the rows that admit all of
+  // them from the lower bound of j1 to the upper bound of j0.
+  int sw_lo, sw_hi, aw_lo, aw_hi;
+  {
+    const int64_t off = (int64_t)a.Nk - a.Nq, right = a.causal ? 0 : a.wr;
+    const int64_t j0 = kw0, j1 = min(kw0 + 31, a.Nk - 1), jf = (int64_t)kw0 + 31;
+    auto clamp_row = [&](int64_t x) { return (int)(x < -64 ? -64 : (x > a.Nq ? a.Nq : x)); };
+    sw_lo = right < 0 ? 0 : clamp_row(j0 - off - right);
+    sw_hi = a.wl < 0 ? a.Nq - 1 : min(a.Nq - 1, clamp_row(j1 - off + a.wl));
+    aw_lo = right < 0 ? 0 : clamp_row(jf - off - right);
+    aw_hi = a.wl < 0 ? a.Nq - 1 : min(a.Nq - 1, clamp_row(j0 - off + a.wl));
+    if (kw0 >= a.Nk) sw_lo = a.Nq;      // no key: every block is skipped
+    if (jf >= a.Nk) aw_lo = a.Nq;       // ragged keys: no block is full
+  }
+  sw_lo = __builtin_amdgcn_readfirstlane(sw_lo);
+  sw_hi = __builtin_amdgcn_readfirstlane(sw_hi);
+  aw_lo = __builtin_amdgcn_readfirstlane(aw_lo);
+  aw_hi = __builtin_amdgcn_readfirstlane(aw_hi);
+  // this wave's keys against the 32-query block starting at row i0: none (0), some (1) or all (2)
+  // of the pairs admitted
   auto block_class = [&](int i0) {
-    const int i1 = min(i0 + 31, a.Nq - 1);
-    const int64_t j1 = min(kw0 + 31, a.Nk - 1);
-    if (kw0 >= a.Nk || i0 >= a.Nq) return 0;
-    if (key_hi(ms, i1) < kw0 || key_lo(ms, i0) > j1) return 0;
-    if (i0 + 31 < a.Nq && key_lo(ms, i1) <= kw0 && kw0 + 31 <= key_hi(ms, i0)) return 2;
+    if (i0 > sw_hi || i0 + 31 < sw_lo) return 0;
+    if (i0 >= aw_lo && i0 + 31 <= aw_hi) return 2;
     return 1;
   };
 
@@ -429,13 +465,20 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) dk[db] = dv[db] = f32x16{};
 
-  if (nsteps > 0) issue(0, 0);
+  int next_h = hk * a.group, next_u = ub;   // the next step to issue
+  int u = ub;                                // query tile of the step being computed
+  if (nsteps > 0) {
+    issue(next_h, next_u, 0);
+    advance(next_h, next_u);
+  }
   for (int n = 0; n < nsteps; ++n) {
     const uint32_t s = (uint32_t)(n & 1) * TILEB;
     const bool more = n + 1 < nsteps;
-    if (more) issue(n + 1, TILEB - s);
+    if (more) {
+      issue(next_h, next_u, TILEB - s);
+      advance(next_h, next_u);
+    }
     barrier_keep(more);
-    const int u = tile_of(n);
     const uint32_t st = sbuf_a + (s ? 2048u : 0u);
     uint32_t qt_base[DB][2], dt_base[DB][2];
     tr_bases<D>(qring_a + s, toff, qt_base);
@@ -493,6 +536,7 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
       }
     }
     barrier_keep(more);
+    if (++u == ue) u = ub;
   }
 
   if (my_key >= a.Nk) return;
