@@ -231,7 +231,7 @@ def main():
         dod = dout.to(dev)
         fwd_step()
         dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
-        ws = fa.bwd_workspace(qd)
+        ws = fa.bwd_workspace(qd, kd)
 
         def step():
             st = fa.bwd_raw(qd, kd, vd, out, dod, lse, dq, dk, dv, ws, w.causal, w.window, scale)

@@ -70,6 +70,31 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
 
+namespace {
+
+// Workgroups over which the dk/dv kernel splits the query heads of each K/V head: doubled (while
+// it divides the group) until the launch has kBwdMinGrid workgroups, so that few K/V heads
+// (MQA, GQA) with short keys still fill the chip.
+constexpr int64_t kBwdMinGrid = 2048;
+int bwd_split(int B, int Hkv, int num_k_tiles, int group) {
+  const int64_t base = (int64_t)B * Hkv * num_k_tiles;
+  int n = 1;
+  while (base * n < kBwdMinGrid && group % (2 * n) == 0) n *= 2;
+  return n;
+}
+
+// fp32 values of the backward workspace: two per query row, then (from a 16-byte boundary) dk
+// and dv partial sums per split when the query heads are split.
+int64_t bwd_rows_floats(int B, int Nq, int Hq) { return (2 * (int64_t)B * Hq * Nq + 3) / 4 * 4; }
+int64_t bwd_workspace_floats(int B, int Nq, int Nk, int Hq, int Hkv, int D) {
+  const int ns = bwd_split(B, Hkv, (Nk + fa::kBwdKRows - 1) / fa::kBwdKRows, Hq / Hkv);
+  int64_t f = bwd_rows_floats(B, Nq, Hq);
+  if (ns > 1) f += 2 * (int64_t)ns * B * Hkv * Nk * D;
+  return f;
+}
+
+}  // namespace
+
 extern "C" {
 
 int fa_version(void) { return 100; }
@@ -81,12 +106,13 @@ const char* fa_status_str(fa_status s) {
     case FA_ERR_SHAPE: return "invalid sizes (B, Nq, Nk, Hq, Hkv >= 1, Hq % Hkv == 0, sizes <= 2^30)";
     case FA_ERR_HEAD_DIM: return "head dimension must be 64 or 128";
     case FA_ERR_WINDOW: return "window bounds must be -1 (unbounded) or >= 0";
-    case FA_ERR_SCALE: return "softmax_scale and descales must be finite and > 0";
+    case FA_ERR_SCALE: return "softmax_scale and descales must be finite and > 0 (fa_bwd: softmax_scale >= 2^-120)";
     case FA_ERR_STRIDES: return "invalid strides or alignment (16-byte aligned, rows must not overlap)";
     case FA_ERR_DTYPE: return "unknown dtype";
     case FA_ERR_DESCALE: return "fp8 e4m3 needs descale_qkv";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_TOO_LARGE: return "one head of a tensor spans 2^31 bytes or more";
+    case FA_ERR_WORKSPACE: return "fa_bwd workspace smaller than fa_bwd_workspace_bytes";
   }
   return "unknown status";
 }
@@ -196,15 +222,22 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* out, float* 
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+size_t fa_bwd_workspace_bytes(int B, int Nq, int Nk, int Hq, int Hkv, int D) {
+  if (check_sizes(B, Nq, Nk, Hq, Hkv, D, -1, -1, FA_F16) != FA_OK) return 0;
+  return (size_t)bwd_workspace_floats(B, Nq, Nk, Hq, Hkv, D) * 4u;
+}
+
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
-                 void* dq, void* dk, void* dv, float* workspace, int B, int Nq, int Nk, int Hq, int Hkv, int D,
-                 const fa_bwd_strides* s, float softmax_scale, int causal, int window_left, int window_right,
-                 fa_dtype dtype, hipStream_t stream) {
+                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int Nq, int Nk, int Hq,
+                 int Hkv, int D, const fa_bwd_strides* s, float softmax_scale, int causal, int window_left,
+                 int window_right, fa_dtype dtype, hipStream_t stream) {
   if (!q || !k || !v || !out || !dout || !lse || !dq || !dk || !dv || !workspace || !s) return FA_ERR_NULL;
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   fa_status st = check_sizes(B, Nq, Nk, Hq, Hkv, D, window_left, window_right, dtype);
   if (st != FA_OK) return st;
-  if (!finite_pos(softmax_scale)) return FA_ERR_SCALE;
+  if ((uint64_t)workspace_bytes < (uint64_t)bwd_workspace_floats(B, Nq, Nk, Hq, Hkv, D) * 4u) return FA_ERR_WORKSPACE;
+  // the workspace holds lse / softmax_scale: bounded scales keep it finite
+  if (!finite_pos(softmax_scale) || softmax_scale < 0x1p-120f) return FA_ERR_SCALE;
   const int64_t str[24] = {s->q_b,  s->q_n,  s->q_h,  s->k_b,  s->k_n,  s->k_h,  s->v_b,  s->v_n,
                            s->v_h,  s->o_b,  s->o_n,  s->o_h,  s->do_b, s->do_n, s->do_h, s->dq_b,
                            s->dq_n, s->dq_h, s->dk_b, s->dk_n, s->dk_h, s->dv_b, s->dv_n, s->dv_h};
@@ -215,21 +248,23 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* out, c
   if ((Nk > 1 && (s->dk_n < D || s->dv_n < D)) || (Hkv > 1 && (s->dk_h < D || s->dv_h < D)) ||
       (B > 1 && (s->dk_b < D || s->dv_b < D)))
     return FA_ERR_STRIDES;
-  const void* ptrs[9] = {q, k, v, out, dout, dq, dk, dv, nullptr};
-  for (int i = 0; i < 8; ++i)
+  const void* ptrs[9] = {q, k, v, out, dout, dq, dk, dv, workspace};
+  for (int i = 0; i < 9; ++i)
     if (!aligned16(ptrs[i])) return FA_ERR_STRIDES;
-  if (((uintptr_t)lse & 3u) || ((uintptr_t)workspace & 3u)) return FA_ERR_STRIDES;
+  if ((uintptr_t)lse & 3u) return FA_ERR_STRIDES;
   if ((int64_t)B * Hq * Nq >= ((int64_t)1 << 31) / 16) return FA_ERR_SHAPE;
 
   fa::BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.o = out; a.dout = dout; a.lse = lse;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.delta = workspace;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.delta = (float*)workspace;
   a.B = B; a.Nq = Nq; a.Nk = Nk; a.Hq = Hq; a.Hkv = Hkv; a.group = Hq / Hkv;
   a.causal = causal ? 1 : 0;
   a.wl = window_left;
   a.wr = window_right;
   a.num_q_tiles = (Nq + fa::kBwdQRows - 1) / fa::kBwdQRows;
   a.num_k_tiles = (Nk + fa::kBwdKRows - 1) / fa::kBwdKRows;
+  a.n_split = bwd_split(B, Hkv, a.num_k_tiles, Hq / Hkv);
+  a.part = a.delta + bwd_rows_floats(B, Nq, Hq);
   a.q_b = s->q_b; a.q_n = s->q_n; a.q_h = s->q_h;
   a.k_b = s->k_b; a.k_n = s->k_n; a.k_h = s->k_h;
   a.v_b = s->v_b; a.v_n = s->v_n; a.v_h = s->v_h;
@@ -243,7 +278,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* out, c
       !span_ok(Nq, s->do_n, D, 2, &a.do_bytes) || !span_ok(Nq, s->dq_n, D, 2, &a.dq_bytes) ||
       !span_ok(Nk, s->dk_n, D, 2, &a.dk_bytes) || !span_ok(Nk, s->dv_n, D, 2, &a.dv_bytes))
     return FA_ERR_TOO_LARGE;
-  if ((int64_t)B * Hkv * a.num_k_tiles >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+  if ((int64_t)B * Hkv * a.num_k_tiles * a.n_split >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
   a.scale = softmax_scale;
   a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
   const hipError_t e = fa::launch_bwd(a, D, dtype, stream);

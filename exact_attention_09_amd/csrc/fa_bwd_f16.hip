@@ -47,9 +47,10 @@ __device__ inline void unpack2(uint32_t w, float& x, float& y) {
 constexpr float kLog2e = 1.44269504088896340736f;
 
 // ---------------------------------------------------------------------------------------------
-// Per query row r = (b, h, i): delta[r] = sum_d dout[b, i, h, d] * out[b, i, h, d], and in the
-// second half of the workspace lse[r] * log2(e) (+inf for a row with no admitted key, so that its
-// p = 2^(s - lse2) is 0). D/8 lanes per row, 16 bytes each.
+// Per query row r = (b, h, i), into the two halves of the workspace: -delta[r], with
+// delta[r] = sum_d dout[b, i, h, d] * out[b, i, h, d], and -lse[r] / softmax_scale, the row's
+// offset in units of raw scores (-inf for a row with no admitted key, so that its p is 0).
+// D/8 lanes per row, 16 bytes each.
 template <class TR, int D>
 __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(BwdArgs a) {
   constexpr int LPR = D / 8;
@@ -75,9 +76,9 @@ __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(BwdArgs a) {
 #pragma unroll
   for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
   if (row < nrows && part == 0) {
-    a.delta[row] = s;
+    a.delta[row] = -s;
     const float l = a.lse[row];
-    a.delta[nrows + row] = l > -INFINITY ? l * kLog2e : INFINITY;
+    a.delta[nrows + row] = l > -INFINITY ? -l / a.scale : -INFINITY;
   }
 }
 
@@ -186,12 +187,12 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(BwdArgs a) {
     qop[ks] = __builtin_amdgcn_raw_buffer_load_b128(q_r, (uint32_t)my_row * (uint32_t)(a.q_n * ES) + (ks * 16 + hl * 8) * ES, 0, 0);
     dop[ks] = __builtin_amdgcn_raw_buffer_load_b128(do_r, (uint32_t)my_row * (uint32_t)(a.do_n * ES) + (ks * 16 + hl * 8) * ES, 0, 0);
   }
-  float lse2 = INFINITY, delta = 0.f;   // rows past the end or with no key: p = 0
+  float lse2 = INFINITY, ndelta = 0.f;   // rows past the end or with no key: p = 0
   if (my_row < a.Nq) {
     const int64_t r = ((int64_t)b * a.Hq + h) * a.Nq + my_row;
     const float l = a.lse[r];
     if (l > -INFINITY) lse2 = l * kLog2e;
-    delta = a.delta[r];
+    ndelta = a.delta[r];                // -delta
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
@@ -276,7 +277,7 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(BwdArgs a) {
         for (int r = 0; r < 16; r += 2) {
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][r], c2, -lse2));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][r + 1], c2, -lse2));
-          dsk[kb][r >> 1] = TR::pack(p0 * (dpt[kb][r] - delta), p1 * (dpt[kb][r + 1] - delta));
+          dsk[kb][r >> 1] = TR::pack(p0 * (dpt[kb][r] + ndelta), p1 * (dpt[kb][r + 1] + ndelta));
         }
       // dQ^T += K^T dS^T
 #pragma unroll
@@ -312,21 +313,23 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NT = 256, BKV = kBwdKRows, BQ = 64, ES = 2;
   constexpr int ROWB = T::ROWB, TILEB = T::TILEB, KS = T::KS, DB = T::DB, QB = BQ / 32;
   constexpr int CH = BQ * (D / 8) / NT;
+  constexpr int NS = 2 * KS, ND = 4 * DB;   // products per 32-query block: S and dP, dV and dK
   __shared__ __attribute__((aligned(16))) char smem[4 * TILEB];   // [Q0 Q1 | dO0 dO1]
   char* const qring = smem;
   char* const dring = smem + 2 * TILEB;
-  // base-2 lse and delta of each slot's 64 query rows (1 KB per row set: the 4-byte LDS-direct load of a
-  // wave covers 256 bytes, the rest is slack)
+  // -lse / scale and -delta of each slot's 64 query rows (1 KB per row set: the 4-byte LDS-direct
+  // load of a wave covers 256 bytes, the rest is slack)
   __shared__ __attribute__((aligned(16))) char sbuf[2 * 2 * 1024];
 
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // (batch, K/V head, key tile); key tiles in increasing order: under a causal mask the first
-  // key tiles meet the most query tiles
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int bkv = L / a.num_k_tiles;
-  const int kt = L - bkv * a.num_k_tiles;
-  const int b = bkv / a.Hkv, hk = bkv - b * a.Hkv;
+  // (batch, K/V head, split of its query heads, key tile) in the forward kernel's launch order,
+  // longest work first under a causal mask: there the first key tiles meet the most query tiles
+  int b, hs, kt;
+  schedule_block(blockIdx.x, gridDim.x, a.num_k_tiles, a.Hkv * a.n_split, a.causal != 0, &b, &hs, &kt);
+  kt = a.num_k_tiles - 1 - kt;
+  const int hk = hs / a.n_split, sp = hs - hk * a.n_split;
+  const int gq = a.group / a.n_split;   // query heads of this workgroup: hk * group + sp * gq + 0 .. gq-1
   const int k0 = kt * BKV;
   const int kw0 = k0 + wave * 32;
   const int my_key = kw0 + l32;
@@ -361,7 +364,7 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
   i_hi = __builtin_amdgcn_readfirstlane(i_hi);
   const int ub = i_lo <= i_hi ? i_lo / BQ : 0, ue = i_lo <= i_hi ? i_hi / BQ + 1 : 0;
   const int nu = ue - ub;                     // query tiles per query head
-  const int nsteps = nu * a.group;
+  const int nsteps = nu * gq;
 
   // this lane's key: K and V as B operands
   i32x4 kop[KS], vop[KS];
@@ -406,18 +409,18 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
   };
   const uint32_t sbuf_a = lds_addr_of(sbuf);
   // loads of the step (query head hh, query tile u) into ring slot `slot` (0 or TILEB): Q and dO
-  // tiles, and the tile's base-2 lse and delta (every wave loads those 64 values into the same
-  // place: 2 loads, same count per wave)
+  // tiles, and the tile's rows of both workspace halves (every wave loads those 64 values into
+  // the same place: 2 loads, same count per wave)
   auto issue = [&](int hh, int u, uint32_t slot) {
     const BufDesc q_d = make_desc((const char*)a.q + (b * a.q_b + hh * a.q_h) * ES, a.q_bytes);
     const BufDesc d_d = make_desc((const char*)a.dout + (b * a.do_b + hh * a.do_h) * ES, a.do_bytes);
     dma(q_d, qgoff, (uint32_t)(u * BQ) * q_rowb, qring_a + slot);
     dma(d_d, dgoff, (uint32_t)(u * BQ) * do_rowb, dring_a + slot);
     const int64_t row0 = ((int64_t)b * a.Hq + hh) * a.Nq;
-    const BufDesc l_d = make_desc(a.delta + (int64_t)a.B * a.Hq * a.Nq + row0, (uint32_t)a.Nq * 4u);
+    const BufDesc w_d = make_desc(a.delta + (int64_t)a.B * a.Hq * a.Nq + row0, (uint32_t)a.Nq * 4u);
     const BufDesc e_d = make_desc(a.delta + row0, (uint32_t)a.Nq * 4u);
     const uint32_t st = sbuf_a + (slot ? 2048u : 0u);
-    dma4(l_d, lane * 4, (uint32_t)(u * BQ) * 4u, st);
+    dma4(w_d, lane * 4, (uint32_t)(u * BQ) * 4u, st);
     dma4(e_d, lane * 4, (uint32_t)(u * BQ) * 4u, st + 1024);
   };
   int roff[KS];
@@ -465,7 +468,7 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) dk[db] = dv[db] = f32x16{};
 
-  int next_h = hk * a.group, next_u = ub;   // the next step to issue
+  int next_h = hk * a.group + sp * gq, next_u = ub;   // the next step to issue
   int u = ub;                                // query tile of the step being computed
   if (nsteps > 0) {
     issue(next_h, next_u, 0);
@@ -480,59 +483,122 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
     }
     barrier_keep(more);
     const uint32_t st = sbuf_a + (s ? 2048u : 0u);
-    uint32_t qt_base[DB][2], dt_base[DB][2];
+    uint32_t qt_base[DB][2], dt_base[DB][2], qr[KS], dr[KS];
     tr_bases<D>(qring_a + s, toff, qt_base);
     tr_bases<D>(dring_a + s, toff, dt_base);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const int i0 = u * BQ + qb * 32;
-      const int cls = __builtin_amdgcn_readfirstlane(block_class(i0));
-      if (cls == 0) continue;
-      // S = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys (one key per lane)
-      f32x16 sc = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        sc = TR::mfma(lds_read_b128(opaque_vbase(qring_a + s + roff[ks]) + qb * 32 * ROWB), kop[ks], sc);
-        dp = TR::mfma(lds_read_b128(opaque_vbase(dring_a + s + roff[ks]) + qb * 32 * ROWB), vop[ks], dp);
-      }
-      // accumulator r holds query i0 + (r/4)*8 + hl*4 + r%4: four groups of four consecutive rows
-      float lse2[16], del[16];
+    for (int ks = 0; ks < KS; ++ks) {
+      qr[ks] = opaque_vbase(qring_a + s + roff[ks]);
+      dr[ks] = opaque_vbase(dring_a + s + roff[ks]);
+    }
+    // Accumulators of block qb start from the rows' offsets: S from -lse / scale (so that
+    // p = 2^(S * scale * log2 e)), dP from -delta (so that ds = p * dP). Accumulator r holds query
+    // i0 + (r/4)*8 + hl*4 + r%4: four groups of four consecutive rows, one 16-byte read each.
+    auto init_acc = [&](int qb, f32x16& sc, f32x16& dp) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const uint32_t at = st + (uint32_t)(qb * 32 + g * 8 + hl * 4) * 4u;
-        const i32x4 lv = lds_read_b128(at), dv4 = lds_read_b128(at + 1024);
+        const i32x4 wv = lds_read_b128(at), nv = lds_read_b128(at + 1024);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          lse2[g * 4 + e] = __int_as_float(lv[e]);
-          del[g * 4 + e] = __int_as_float(dv4[e]);
+          sc[g * 4 + e] = __int_as_float(wv[e]);
+          dp[g * 4 + e] = __int_as_float(nv[e]);
         }
       }
-      if (cls == 1) {
+    };
+    // Operand and product m of block qb's sequences. S/dP (NS of them): k-slot m / 2, even m
+    // S += Q K^T, odd m dP += dO V^T. dV/dK (ND of them): half m / (2 DB), column block
+    // (m / 2) % DB, even m dV^T += dO^T P, odd m dK^T += Q^T dS.
+    auto sdp_operand = [&](int qb, int m) { return lds_read_b128((m % 2 ? dr : qr)[m / 2] + qb * 32 * ROWB); };
+    auto sdp_mfma = [&](int m, const i32x4& x, f32x16& sc, f32x16& dp) {
+      if (m % 2 == 0) sc = TR::mfma(x, kop[m / 2], sc);
+      else dp = TR::mfma(x, vop[m / 2], dp);
+    };
+    auto dvdk_operand = [&](int qb, int m) {
+      return tr_operand<D>(m % 2 ? qt_base : dt_base, qb, m / (2 * DB), (m / 2) % DB);
+    };
+    auto dvdk_mfma = [&](int m, const i32x4& x, const uint32_t (&pk)[8], const uint32_t (&dsk)[8]) {
+      const int h4 = 4 * (m / (2 * DB)), db = (m / 2) % DB;
+      if (m % 2 == 0) dv[db] = TR::mfma(x, i32x4{(int)pk[h4], (int)pk[h4 + 1], (int)pk[h4 + 2], (int)pk[h4 + 3]}, dv[db]);
+      else dk[db] = TR::mfma(x, i32x4{(int)dsk[h4], (int)dsk[h4 + 1], (int)dsk[h4 + 2], (int)dsk[h4 + 3]}, dk[db]);
+    };
+    // softmax pair pi of a block: p = 2^(S c2), ds = p dP, both packed to the MFMA type
+    auto pair = [&](const f32x16& sc, const f32x16& dp, int pi, uint32_t (&pk)[8], uint32_t (&dsk)[8]) {
+      const float p0 = __builtin_amdgcn_exp2f(sc[2 * pi] * c2), p1 = __builtin_amdgcn_exp2f(sc[2 * pi + 1] * c2);
+      pk[pi] = TR::pack(p0, p1);
+      dsk[pi] = TR::pack(p0 * dp[2 * pi], p1 * dp[2 * pi + 1]);
+    };
+
+    const int i0 = u * BQ;
+    const int c0 = __builtin_amdgcn_readfirstlane(block_class(i0));
+    const int c1 = __builtin_amdgcn_readfirstlane(block_class(i0 + 32));
+    if (D == 128 && c0 == 2 && c1 == 2) {
+      // Both blocks full: one sequence S/dP(0), S/dP(1), dV/dK(0), dV/dK(1) in which the softmax
+      // of block 0 runs beside S/dP(1) and that of block 1 beside dV/dK(0). Operands are read
+      // PF products ahead. At D = 128 the kernel runs one wave per SIMD, and this overlap within
+      // the wave measured 8% faster; at D = 64 two waves share each SIMD and overlap each other,
+      // and the sequence (whose registers would no longer allow two waves) measured slower.
+      constexpr int NE = 2 * (NS + ND), PF = 2, GS = NS / 8, GD = ND / 8;
+      f32x16 sc0, dp0, sc1, dp1;
+      uint32_t pk0[8], dsk0[8], pk1[8], dsk1[8];
+      i32x4 opnd[NE];
+      auto read_op = [&](int e) {
+        if (e < NS) opnd[e] = sdp_operand(0, e);
+        else if (e < 2 * NS) opnd[e] = sdp_operand(1, e - NS);
+        else if (e < 2 * NS + ND) opnd[e] = dvdk_operand(0, e - 2 * NS);
+        else opnd[e] = dvdk_operand(1, e - 2 * NS - ND);
+      };
+      init_acc(0, sc0, dp0);
+      init_acc(1, sc1, dp1);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = i0 + (r >> 2) * 8 + hl * 4 + (r & 3);
-          const bool ok = i < a.Nq && my_key < a.Nk && key_lo(ms, i) <= my_key && my_key <= key_hi(ms, i);
-          sc[r] = ok ? sc[r] : -INFINITY;
+      for (int e = 0; e < PF; ++e) read_op(e);
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<0, NE>([&](auto E) {
+        constexpr int e = decltype(E)::value;
+        if constexpr (e + PF < NE) read_op(e + PF);
+        if (e < NS) {
+          sdp_mfma(e, opnd[e], sc0, dp0);
+        } else if (e < 2 * NS) {
+          sdp_mfma(e - NS, opnd[e], sc1, dp1);
+          if ((e - NS) % GS == GS - 1) {
+            const int pi = (e - NS) / GS;
+            pair(sc0, dp0, pi, pk0, dsk0);
+            asm volatile("" ::"v"(pk0[pi]), "v"(dsk0[pi]));
+          }
+        } else if (e < 2 * NS + ND) {
+          dvdk_mfma(e - 2 * NS, opnd[e], pk0, dsk0);
+          if ((e - 2 * NS) % GD == GD - 1) {
+            const int pi = (e - 2 * NS) / GD;
+            pair(sc1, dp1, pi, pk1, dsk1);
+            asm volatile("" ::"v"(pk1[pi]), "v"(dsk1[pi]));
+          }
+        } else {
+          dvdk_mfma(e - 2 * NS - ND, opnd[e], pk1, dsk1);
         }
-      }
-      uint32_t pk[8], dsk[8];
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    } else {
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r], c2, -lse2[r]));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[r + 1], c2, -lse2[r + 1]));
-        pk[r >> 1] = TR::pack(p0, p1);
-        dsk[r >> 1] = TR::pack(p0 * (dp[r] - del[r]), p1 * (dp[r + 1] - del[r + 1]));
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS (k = the block's 32 queries, two halves of 16)
+      for (int qb = 0; qb < QB; ++qb) {
+        const int cls = qb == 0 ? c0 : c1;
+        if (cls == 0) continue;
+        f32x16 sc, dp;
+        init_acc(qb, sc, dp);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const i32x4 pop = i32x4{(int)pk[4 * half], (int)pk[4 * half + 1], (int)pk[4 * half + 2], (int)pk[4 * half + 3]};
-        const i32x4 dsop = i32x4{(int)dsk[4 * half], (int)dsk[4 * half + 1], (int)dsk[4 * half + 2], (int)dsk[4 * half + 3]};
+        for (int m = 0; m < NS; ++m) sdp_mfma(m, sdp_operand(qb, m), sc, dp);
+        if (cls == 1) {
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          dv[db] = TR::mfma(tr_operand<D>(dt_base, qb, half, db), pop, dv[db]);
-          dk[db] = TR::mfma(tr_operand<D>(qt_base, qb, half, db), dsop, dk[db]);
+          for (int r = 0; r < 16; ++r) {
+            const int i = i0 + qb * 32 + (r >> 2) * 8 + hl * 4 + (r & 3);
+            const bool ok = i < a.Nq && my_key < a.Nk && key_lo(ms, i) <= my_key && my_key <= key_hi(ms, i);
+            sc[r] = ok ? sc[r] : -INFINITY;
+          }
         }
+        uint32_t pk[8], dsk[8];
+#pragma unroll
+        for (int pi = 0; pi < 8; ++pi) pair(sc, dp, pi, pk, dsk);
+#pragma unroll
+        for (int m = 0; m < ND; ++m) dvdk_mfma(m, dvdk_operand(qb, m), pk, dsk);
       }
     }
     barrier_keep(more);
@@ -540,6 +606,20 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
   }
 
   if (my_key >= a.Nk) return;
+  if (a.n_split > 1) {
+    // fp32 partial sums; fa_bwd_reduce_kernel adds the splits and scales dk
+    const int64_t slab = (int64_t)a.n_split * a.B * a.Hkv * a.Nk * D;
+    float* pk_row = a.part + ((((int64_t)sp * a.B + b) * a.Hkv + hk) * a.Nk + my_key) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int col = db * 32 + q4 * 8 + hl * 4;
+        *(f32x4*)(pk_row + col) = f32x4{dk[db][4 * q4], dk[db][4 * q4 + 1], dk[db][4 * q4 + 2], dk[db][4 * q4 + 3]};
+        *(f32x4*)(pk_row + slab + col) = f32x4{dv[db][4 * q4], dv[db][4 * q4 + 1], dv[db][4 * q4 + 2], dv[db][4 * q4 + 3]};
+      }
+    return;
+  }
   const uint32_t dk_rowb = (uint32_t)(a.dk_n * ES), dv_rowb = (uint32_t)(a.dv_n * ES);
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -556,13 +636,42 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// dk, dv = the sum over the n_split query-head splits of the fp32 partials (in split order, so the
+// result does not depend on timing), dk times softmax_scale; 4 columns per thread.
+template <class TR, int D>
+__global__ void __launch_bounds__(256) fa_bwd_reduce_kernel(BwdArgs a) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per = (int64_t)a.B * a.Hkv * a.Nk * D;   // floats of one split
+  if (gid * 4 >= per) return;
+  const int64_t row = gid / (D / 4);
+  const int col = (int)(gid - row * (D / 4)) * 4;
+  const int key = (int)(row % a.Nk);
+  const int64_t bh = row / a.Nk;
+  const int hk = (int)(bh % a.Hkv), b = (int)(bh / a.Hkv);
+  f32x4 sk = f32x4{}, sv = f32x4{};
+  const int64_t slab = (int64_t)a.n_split * per;
+  for (int s = 0; s < a.n_split; ++s) {
+    sk += *(const f32x4*)(a.part + s * per + gid * 4);
+    sv += *(const f32x4*)(a.part + slab + s * per + gid * 4);
+  }
+  const uint32_t k0 = TR::pack(sk[0] * a.scale, sk[1] * a.scale), k1 = TR::pack(sk[2] * a.scale, sk[3] * a.scale);
+  const uint32_t v0 = TR::pack(sv[0], sv[1]), v1 = TR::pack(sv[2], sv[3]);
+  *(i32x2*)((char*)a.dk + (b * a.dk_b + (int64_t)key * a.dk_n + hk * a.dk_h + col) * 2) = i32x2{(int)k0, (int)k1};
+  *(i32x2*)((char*)a.dv + (b * a.dv_b + (int64_t)key * a.dv_n + hk * a.dv_h + col) * 2) = i32x2{(int)v0, (int)v1};
+}
+
+// ---------------------------------------------------------------------------------------------
 template <class TR, int D>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.Hq * a.Nq;
   const int64_t delta_blocks = (rows * (D / 8) + 255) / 256;
   hipLaunchKernelGGL((fa_bwd_delta_kernel<TR, D>), dim3((unsigned)delta_blocks), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<TR, D>), dim3((unsigned)((int64_t)a.B * a.Hkv * a.num_k_tiles)), dim3(256), 0,
-                     stream, a);
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<TR, D>),
+                     dim3((unsigned)((int64_t)a.B * a.Hkv * a.n_split * a.num_k_tiles)), dim3(256), 0, stream, a);
+  if (a.n_split > 1) {
+    const int64_t quads = (int64_t)a.B * a.Hkv * a.Nk * (D / 4);
+    hipLaunchKernelGGL((fa_bwd_reduce_kernel<TR, D>), dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, stream, a);
+  }
   hipLaunchKernelGGL((fa_bwd_dq_kernel<TR, D>), dim3((unsigned)((int64_t)a.B * a.Hq * a.num_q_tiles)), dim3(256), 0,
                      stream, a);
   return hipGetLastError();

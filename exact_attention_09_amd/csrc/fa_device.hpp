@@ -5,11 +5,27 @@
 
 namespace fa {
 
+// f(Int<0>{}), ..., f(Int<N-1>{}): a loop whose index is a compile-time constant in every trip
+// (for long bodies the unroller may otherwise keep a loop, and arrays indexed by its counter
+// then live in scratch memory).
+template <int I>
+struct Int {
+  static constexpr int value = I;
+};
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(Int<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -29,33 +45,42 @@ __device__ inline int xcd_remap(int id, int n) {
   return xcd * per + (xcd < rem ? xcd : rem) + k;
 }
 
-// Which (batch, query head, query tile) workgroup `id` of a launch of n computes. Blocks are dealt
-// round-robin over the 8 XCDs; xcd_remap turns that into one contiguous range of the sequence
-// below per XCD. Heads are enumerated batch-major, and inside a batch the query heads sharing a
-// K/V head are consecutive. Without a causal mask the sequence is head by head (a head's K/V
-// then stays in one XCD's L2). Under a causal mask query tiles differ in length by up to the
-// number of tiles, so the sequence goes by chunks of kChunk heads (one K/V head under 4-way
-// GQA), longest tiles of the chunk first: the chunks in flight on an XCD keep its L2 working
-// set small, and the longest work of each chunk starts first, which keeps the launch's tail
-// short.
-__device__ inline void schedule_block(int id, int n, int num_q_tiles, int Hq, bool causal, int* b, int* h, int* qt) {
+// Which (batch, head, tile) workgroup `id` of a launch of n = (batch x heads) x num_tiles
+// computes. Heads are enumerated batch-major (inside a batch the query heads sharing a K/V head
+// are consecutive); under a causal mask tile t is the longest of its head when t = num_tiles - 1
+// and the shortest when t = 0. Blocks are dealt round-robin over the 8 XCDs.
+//  * No causal mask: head by head, each XCD one contiguous range of heads (xcd_remap), so a
+//    head's K/V stays in one XCD's L2.
+//  * Causal, heads a multiple of 8: each XCD takes a contiguous range of whole heads and goes
+//    through them by chunks of up to kChunk heads (a divisor of its head count; one K/V head
+//    under 4-way GQA), longest tiles of the chunk first: the chunk in flight keeps the XCD's L2
+//    working set small, every XCD gets the same mix of long and short tiles, and the longest
+//    work starts first, which keeps the launch's tail short.
+//  * Causal otherwise: longest tiles of every head first, consecutive ids on different XCDs.
+__device__ inline void schedule_block(int id, int n, int num_tiles, int H, bool causal, int* b, int* h, int* t) {
   constexpr int kChunk = 4;
-  const int L = xcd_remap(id, n);
-  const int n_bh = n / num_q_tiles;
+  const int n_bh = n / num_tiles;
   int bh;
-  if (causal && n_bh % kChunk == 0) {
-    const int per = kChunk * num_q_tiles;
+  if (!causal) {
+    const int L = xcd_remap(id, n);
+    bh = L / num_tiles;
+    *t = L - bh * num_tiles;
+  } else if (n_bh % 8 == 0) {
+    const int hx = n_bh / 8;   // heads per XCD
+    const int c = hx % kChunk == 0 ? kChunk : (hx % 2 == 0 ? 2 : 1);
+    const int L = xcd_remap(id, n);
+    const int per = c * num_tiles;
     const int chunk = L / per, r = L - chunk * per;
-    const int rank = r / kChunk;
-    bh = chunk * kChunk + (r - rank * kChunk);
-    *qt = num_q_tiles - 1 - rank;
+    const int rank = r / c;
+    bh = chunk * c + (r - rank * c);
+    *t = num_tiles - 1 - rank;
   } else {
-    bh = L / num_q_tiles;
-    *qt = L - bh * num_q_tiles;
-    if (causal) *qt = num_q_tiles - 1 - *qt;
+    const int rank = id / n_bh;
+    bh = id - rank * n_bh;
+    *t = num_tiles - 1 - rank;
   }
-  *b = bh / Hq;
-  *h = bh - *b * Hq;
+  *b = bh / H;
+  *h = bh - *b * H;
 }
 
 // Value of x held by lane l ^ 32, combined with x: max or sum over the lane pair.

@@ -36,12 +36,14 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;          // [2, B, Hq, Nq] workspace: rowsum(dout * out), then lse * log2(e)
-                         // (+inf for rows with no admitted key)
+  float* delta;          // [2, B, Hq, Nq] workspace: -rowsum(dout * out), then -lse / scale
+                         // (-inf for rows with no admitted key)
   int B, Nq, Nk, Hq, Hkv, group;
   int causal, wl, wr;
   int num_q_tiles;       // of the dq kernel's query tiles
   int num_k_tiles;       // of the dk/dv kernel's key tiles
+  int n_split;           // dk/dv workgroups per (K/V head, key tile), each for group / n_split query heads
+  float* part;           // n_split > 1: fp32 partial dk, then dv, [n_split, B, Hkv, Nk, D] each
   int64_t q_b, q_n, q_h, k_b, k_n, k_h, v_b, v_n, v_h, o_b, o_n, o_h;
   int64_t do_b, do_n, do_h, dq_b, dq_n, dq_h, dk_b, dk_n, dk_h, dv_b, dv_n, dv_h;
   uint32_t q_bytes, k_bytes, v_bytes, o_bytes, do_bytes, dq_bytes, dk_bytes, dv_bytes;

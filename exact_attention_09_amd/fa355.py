@@ -20,7 +20,7 @@ _DTYPE_CODE = {torch.float16: FA_F16, torch.bfloat16: FA_BF16, torch.float8_e4m3
 _OUT_DTYPE = {FA_F16: torch.float16, FA_BF16: torch.bfloat16, FA_FP8_E4M3: torch.bfloat16}
 
 # Every symbol include/fa355.h declares.
-EXPORTED = ("fa_fwd", "fa_bwd", "fa_status_str", "fa_fwd_plan", "fa_kv_tile_range", "fa_version")
+EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str", "fa_fwd_plan", "fa_kv_tile_range", "fa_version")
 
 
 class FaStrides(ctypes.Structure):
@@ -61,8 +61,10 @@ def load() -> ctypes.CDLL:
                            c_int, c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(FaStrides),
                            c_float, c_int, c_int, c_int, c_int, c_void_p, ctypes.POINTER(c_float)]
     lib.fa_bwd.restype = c_int
-    lib.fa_bwd.argtypes = [c_void_p] * 10 + [c_int] * 6 + [ctypes.POINTER(FaBwdStrides), c_float, c_int, c_int, c_int,
-                                              c_int, c_void_p]
+    lib.fa_bwd.argtypes = [c_void_p] * 10 + [ctypes.c_size_t] + [c_int] * 6 + [ctypes.POINTER(FaBwdStrides), c_float,
+                                                                   c_int, c_int, c_int, c_int, c_void_p]
+    lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_bwd_workspace_bytes.argtypes = [c_int] * 6
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_status_str.argtypes = [c_int]
     lib.fa_fwd_plan.restype = c_int
@@ -160,7 +162,7 @@ def kv_tile_range(Nq, Nk, causal, window, block_n, row_begin, row_end):
 def bwd_raw(q, k, v, out, dout, lse, dq, dk, dv, workspace, causal=False, window=(-1, -1), softmax_scale=None,
             stream=None) -> int:
     """Call fa_bwd on caller-provided tensors; returns the status code (0 = ok) without raising.
-    ``workspace``: fp32 device tensor of 2 * B * Hq * Nq elements (see ``bwd_workspace``)."""
+    ``workspace``: device tensor of at least fa_bwd_workspace_bytes bytes (see ``bwd_workspace``)."""
     lib = load()
     code = _DTYPE_CODE.get(q.dtype)
     if code is None:
@@ -178,14 +180,20 @@ def bwd_raw(q, k, v, out, dout, lse, dq, dk, dv, workspace, causal=False, window
         setattr(st, name + "_n", t.stride(1))
         setattr(st, name + "_h", t.stride(2))
     return lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, Nq, Nk, Hq, Hkv, D,
+                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+                      workspace.numel() * workspace.element_size(), B, Nq, Nk, Hq, Hkv, D,
                       ctypes.byref(st), scale, int(bool(causal)), int(window[0]), int(window[1]), code, stream)
 
 
-def bwd_workspace(q):
-    """The fp32 workspace fa_bwd needs for queries q [B, Nq, Hq, D]: 2 * B * Hq * Nq floats."""
-    B, Nq, Hq, _ = q.shape
-    return torch.empty(2, B, Hq, Nq, dtype=torch.float32, device=q.device)
+def bwd_workspace(q, k):
+    """The device workspace fa_bwd needs for queries q [B, Nq, Hq, D] and keys k [B, Nk, Hkv, D]
+    (fa_bwd_workspace_bytes of the sizes, as an fp32 tensor)."""
+    B, Nq, Hq, D = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    nbytes = load().fa_bwd_workspace_bytes(B, Nq, Nk, Hq, Hkv, D)
+    if nbytes == 0:
+        raise ValueError(f"invalid sizes for the backward pass: q {tuple(q.shape)}, k {tuple(k.shape)}")
+    return torch.empty(nbytes // 4, dtype=torch.float32, device=q.device)
 
 
 def bwd(q, k, v, out, dout, lse, causal=False, window=(-1, -1), softmax_scale=None):
@@ -197,7 +205,7 @@ def bwd(q, k, v, out, dout, lse, causal=False, window=(-1, -1), softmax_scale=No
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)
-    status = bwd_raw(q, k, v, out, dout, lse, dq, dk, dv, bwd_workspace(q), causal, window, softmax_scale)
+    status = bwd_raw(q, k, v, out, dout, lse, dq, dk, dv, bwd_workspace(q, k), causal, window, softmax_scale)
     if status != 0:
         raise FaError(status, status_str(status))
     return dq, dk, dv

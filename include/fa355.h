@@ -60,7 +60,8 @@ typedef enum fa_status {
   FA_ERR_DTYPE = 7,     /* unknown dtype                                                           */
   FA_ERR_DESCALE = 8,   /* FA_FP8_E4M3 without descale_qkv                                         */
   FA_ERR_LAUNCH = 9,    /* the kernel launch failed (HIP error; e.g. no device)                    */
-  FA_ERR_TOO_LARGE = 10 /* one head's span of q, k, v or out reaches 2^31 bytes                    */
+  FA_ERR_TOO_LARGE = 10, /* one head's span of q, k, v or out reaches 2^31 bytes                   */
+  FA_ERR_WORKSPACE = 11  /* fa_bwd: workspace_bytes below fa_bwd_workspace_bytes of the sizes       */
 } fa_status;
 
 /* Element strides (not bytes) of the batch, seqlen and head axes; the headdim stride is 1. */
@@ -125,19 +126,30 @@ typedef struct fa_bwd_strides {
  * dq                 device, [B, Nq, Hq, D];  dk, dv: device, [B, Nk, Hkv, D]; dtype storage.
  *                    Written in full (every row, including rows with no admitted key: zero).
  *                    Must not alias each other or the inputs.
- * workspace          device fp32 workspace of 2 * B * Hq * Nq floats, 4-byte aligned: the pass
- *                    writes rowsum(dout * out) per query row into the first half and lse * log2(e)
- *                    into the second, then reads them back. The caller allocates it; its contents
- *                    on entry do not matter.
+ * workspace          device scratch of workspace_bytes >= fa_bwd_workspace_bytes(B, Nq, Nk, Hq,
+ *                    Hkv, D) bytes (else FA_ERR_WORKSPACE), 16-byte aligned, owned by the caller;
+ *                    its contents on entry do not matter. It holds two fp32 values per query row
+ *                    (-rowsum(dout * out) and -lse / softmax_scale) and, when the query heads of
+ *                    a K/V head are split over several workgroups (few K/V heads and short keys),
+ *                    their fp32 partial sums of dk and dv, added up in a fixed order.
+ * softmax_scale      finite and at least 2^-120 (else FA_ERR_SCALE), so that lse / softmax_scale
+ *                    stays finite.
  * dtype              FA_F16 or FA_BF16 (FA_FP8_E4M3 returns FA_ERR_DTYPE).
  * Other arguments, validation, ownership and asynchrony as for fa_fwd. Deterministic: no
  * atomics; the same inputs give bitwise the same gradients.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
-                 const float* lse, void* dq, void* dk, void* dv, float* workspace,
+                 const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                  int B, int Nq, int Nk, int Hq, int Hkv, int D, const fa_bwd_strides* strides,
                  float softmax_scale, int causal, int window_left, int window_right,
                  fa_dtype dtype, hipStream_t stream);
+
+/*
+ * fa_bwd_workspace_bytes — bytes of device workspace fa_bwd needs for these sizes (a multiple of
+ * 4); 0 when the sizes are invalid for fa_bwd (then fa_bwd reports the reason). Pure host
+ * function: no device call.
+ */
+size_t fa_bwd_workspace_bytes(int B, int Nq, int Nk, int Hq, int Hkv, int D);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_status_str(fa_status s);

@@ -111,3 +111,24 @@ def test_bwd_c3_shape_sampled_head():
     sl = lambda t: t[b:b + 1, :, h:h + 1, :]
     ref = attention_bwd_fp64(decode(sl(q)), decode(sl(k)), decode(sl(v)), decode(sl(do)), 0.125, True, (-1, -1))
     check(tuple(sl(t) for t in got), ref, torch.float16, "c3 head (2, 17)")
+
+
+@pytest.mark.parametrize("wl", ["causal_b4_h32_n4096_d64_f16", "gqa_b1_hq32_hkv8_n16384_d128_bf16",
+                                "mqa_b1_hq32_hkv1_n16384_d128_bf16"])
+def test_bwd_benchmark_shape_tail(wl):
+    """The benchmark's shapes and launch (the MQA one splits each K/V head's query heads over 16
+    workgroups and adds the partial sums). Under the causal mask the last T keys receive
+    gradient only from the last T query rows, so the oracle run on those rows alone (all keys,
+    bottom-right alignment keeps every row's mask) gives exact dq for those rows and exact dk, dv
+    for those keys."""
+    from exact_attention_09_amd.inputs import WORKLOADS, make_inputs
+    w = WORKLOADS[wl]
+    assert w.causal and w.window == (-1, -1) and w.Nq == w.Nk
+    q, k, v, _ = make_inputs(w, 0)
+    g = torch.Generator().manual_seed(1)
+    do = torch.randn(w.B, w.Nq, w.Hq, w.D, generator=g).to(q.dtype)
+    scale = w.softmax_scale()
+    got = gpu_grads(q, k, v, do, True, (-1, -1), scale)
+    T = 64
+    ref = attention_bwd_fp64(decode(q[:, -T:]), decode(k), decode(v), decode(do[:, -T:]), scale, True, (-1, -1))
+    check((got[0][:, -T:], got[1][:, -T:], got[2][:, -T:]), (ref[0], ref[1][:, -T:], ref[2][:, -T:]), q.dtype, wl)
