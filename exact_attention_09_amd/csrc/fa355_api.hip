@@ -215,8 +215,77 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* out, float* 
   const double log2e = 1.4426950408889634074;
   a.scale_log2 = (float)((double)softmax_scale * dq * dk * log2e);
   a.out_scale = dtype == FA_FP8_E4M3 ? dv : 1.f;
+  a.cu_q = a.cu_k = nullptr;
+  a.total_q = a.total_k = 0;
   const fa::TileShape ts = fa::tile_shape(D, dtype);
   a.num_q_tiles = (Nq + ts.block_m - 1) / ts.block_m;
+  const int64_t grid = (int64_t)B * Hq * a.num_q_tiles;
+  const hipError_t e = fa::launch_fwd(a, D, dtype, grid, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse, const int32_t* cu_seqlens_q,
+                        const int32_t* cu_seqlens_k, int B, int total_q, int total_k, int max_seqlen_q, int Hq,
+                        int Hkv, int D, const fa_varlen_strides* s, float softmax_scale, int causal,
+                        int window_left, int window_right, fa_dtype dtype, hipStream_t stream,
+                        const float* descale_qkv) {
+  if (!q || !k || !v || !out || !s || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULL;
+  // the sizes as one dense launch of B sequences of max_seqlen_q queries
+  fa_status st = check_sizes(B, max_seqlen_q, total_k, Hq, Hkv, D, window_left, window_right, dtype);
+  if (st != FA_OK) return st;
+  if (total_q < 1 || total_q > kMaxSeq || max_seqlen_q > total_q) return FA_ERR_SHAPE;
+  if (!finite_pos(softmax_scale)) return FA_ERR_SCALE;
+  float dq = 1.f, dk = 1.f, dv = 1.f;
+  if (dtype == FA_FP8_E4M3) {
+    if (!descale_qkv) return FA_ERR_DESCALE;
+    dq = descale_qkv[0];
+    dk = descale_qkv[1];
+    dv = descale_qkv[2];
+    if (!finite_pos(dq) || !finite_pos(dk) || !finite_pos(dv)) return FA_ERR_SCALE;
+  }
+  const int es = elem_bytes(dtype);
+  const int oes = 2;
+  const int64_t in_str[6] = {s->q_n, s->q_h, s->k_n, s->k_h, s->v_n, s->v_h};
+  for (int i = 0; i < 6; ++i)
+    if (in_str[i] < 0 || (in_str[i] * es) % 16 != 0) return FA_ERR_STRIDES;
+  if (s->o_n < 0 || s->o_h < 0 || (s->o_n * oes) % 16 != 0 || (s->o_h * oes) % 16 != 0) return FA_ERR_STRIDES;
+  if ((total_q > 1 && s->o_n < D) || (Hq > 1 && s->o_h < D)) return FA_ERR_STRIDES;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || ((uintptr_t)lse & 3u)) return FA_ERR_STRIDES;
+  if (((uintptr_t)cu_seqlens_q & 3u) || ((uintptr_t)cu_seqlens_k & 3u)) return FA_ERR_STRIDES;
+
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = out;
+  a.lse = lse;
+  a.B = B;
+  a.Nq = max_seqlen_q;
+  a.Nk = total_k;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.group = Hq / Hkv;
+  a.causal = causal ? 1 : 0;
+  a.wl = window_left;
+  a.wr = window_right;
+  a.q_b = a.k_b = a.v_b = a.o_b = 0;
+  a.q_n = s->q_n; a.q_h = s->q_h;
+  a.k_n = s->k_n; a.k_h = s->k_h;
+  a.v_n = s->v_n; a.v_h = s->v_h;
+  a.o_n = s->o_n; a.o_h = s->o_h;
+  // every sequence is a row range of the packed tensors: bound the whole packed span
+  if (!span_ok(total_q, s->q_n, D, es, &a.q_bytes) || !span_ok(total_k, s->k_n, D, es, &a.k_bytes) ||
+      !span_ok(total_k, s->v_n, D, es, &a.v_bytes) || !span_ok(total_q, s->o_n, D, oes, &a.o_bytes))
+    return FA_ERR_TOO_LARGE;
+  const double log2e = 1.4426950408889634074;
+  a.scale_log2 = (float)((double)softmax_scale * dq * dk * log2e);
+  a.out_scale = dtype == FA_FP8_E4M3 ? dv : 1.f;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  const fa::TileShape ts = fa::tile_shape(D, dtype);
+  a.num_q_tiles = (max_seqlen_q + ts.block_m - 1) / ts.block_m;
   const int64_t grid = (int64_t)B * Hq * a.num_q_tiles;
   const hipError_t e = fa::launch_fwd(a, D, dtype, grid, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;

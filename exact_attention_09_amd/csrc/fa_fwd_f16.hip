@@ -73,30 +73,32 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   schedule_block(blockIdx.x, gridDim.x, a.num_q_tiles, a.Hq, a.causal != 0, &b, &h, &qt);
   const int hk = h / a.group;                    // MQA/GQA: K/V head of this query head
   const int q0 = qt * BM;
+  const SeqView sv = seq_view(a, b, h, D, ES, ES);
+  if (q0 >= sv.Nq) return;                       // past the end of a shorter packed sequence
 
-  const MaskSpec ms{a.Nq, a.Nk, a.causal, a.wl, a.wr};
+  const MaskSpec ms{sv.Nq, sv.Nk, a.causal, a.wl, a.wr};
 
-  const char* qb = (const char*)a.q + (b * a.q_b + h * a.q_h) * ES;
-  const char* kbp = (const char*)a.k + (b * a.k_b + hk * a.k_h) * ES;
-  const char* vbp = (const char*)a.v + (b * a.v_b + hk * a.v_h) * ES;
-  char* ob = (char*)a.o + (b * a.o_b + h * a.o_h) * ES;
-  const __amdgpu_buffer_rsrc_t q_r = make_rsrc(qb, a.q_bytes);
-  const __amdgpu_buffer_rsrc_t o_r = make_rsrc(ob, a.o_bytes);
+  const char* qb = (const char*)a.q + (sv.q0 + h * a.q_h) * ES;
+  const char* kbp = (const char*)a.k + (sv.k0 + hk * a.k_h) * ES;
+  const char* vbp = (const char*)a.v + (sv.v0 + hk * a.v_h) * ES;
+  char* ob = (char*)a.o + (sv.o0 + h * a.o_h) * ES;
+  const __amdgpu_buffer_rsrc_t q_r = make_rsrc(qb, sv.q_bytes);
+  const __amdgpu_buffer_rsrc_t o_r = make_rsrc(ob, sv.o_bytes);
   const uint32_t q_rowb = (uint32_t)(a.q_n * ES), k_rowb = (uint32_t)(a.k_n * ES);
   const uint32_t v_rowb = (uint32_t)(a.v_n * ES), o_rowb = (uint32_t)(a.o_n * ES);
 
   // ---- K/V tiles this workgroup visits, and this wave's rows
-  const int wg_last = min(q0 + BM, a.Nq) - 1;
+  const int wg_last = min(q0 + BM, sv.Nq) - 1;
   int tb, te;
   tile_range(ms, q0, wg_last, BN, &tb, &te);
   const int w0 = q0 + wave * 32;
-  const bool wave_live = w0 < a.Nq;
-  const int w1 = min(w0 + 31, a.Nq - 1);
+  const bool wave_live = w0 < sv.Nq;
+  const int w1 = min(w0 + 31, sv.Nq - 1);
   // Key bounds of the wave's first and last rows, clamped to [-1, Nk] (wave-uniform scalars).
   // Each row admits an interval of keys and both ends grow with the row, so the tiles holding
   // an admitted key for some row of the wave form an interval [jlo, jhi), and the tiles admitted
   // for every row another one, [flo, fhi), inside it.
-  auto clamp_key = [&](int64_t x) { return (int)(x < -1 ? -1 : (x > a.Nk ? a.Nk : x)); };
+  auto clamp_key = [&](int64_t x) { return (int)(x < -1 ? -1 : (x > sv.Nk ? sv.Nk : x)); };
   const int wlo0 = __builtin_amdgcn_readfirstlane(clamp_key(key_lo(ms, w0)));
   const int wlo1 = __builtin_amdgcn_readfirstlane(clamp_key(key_lo(ms, w1)));
   const int whi0 = __builtin_amdgcn_readfirstlane(clamp_key(key_hi(ms, w0)));
@@ -126,7 +128,7 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
     kgoff[i] = (uint32_t)row * k_rowb + ((pc ^ k_swz<ROWB>(row)) << 4);
     vgoff[i] = (uint32_t)row * v_rowb + ((pc ^ v_swz<ROWB>(row)) << 4);
   }
-  const BufDesc k_d = make_desc(kbp, a.k_bytes), v_d = make_desc(vbp, a.v_bytes);
+  const BufDesc k_d = make_desc(kbp, sv.k_bytes), v_d = make_desc(vbp, sv.v_bytes);
   const uint32_t kring_a = lds_addr_of(kring), vring_a = lds_addr_of(vring);
   // The CH loads of one tile: soff is the tile's byte offset in the head, lds its ring slot.
   auto dma = [&](const BufDesc& d, const uint32_t* goff, uint32_t soff, uint32_t lds) {
@@ -360,7 +362,7 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   }
 
   // ---- epilogue: O / l, lse = (m + log2 l) * ln 2
-  if (!wave_live || my_row >= a.Nq) return;
+  if (!wave_live || my_row >= sv.Nq) return;
   const float l_tot = pair_sum(l);
   const float inv = l_tot > 0.f ? a.out_scale / l_tot : 0.f;
 #pragma unroll
@@ -374,7 +376,7 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
     }
   if (a.lse != nullptr && hl == 0) {
     const float lse = l_tot > 0.f ? (m + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-    a.lse[((int64_t)b * a.Hq + h) * a.Nq + my_row] = lse;
+    a.lse[sv.lse0 + my_row] = lse;
   }
 }
 

@@ -23,7 +23,58 @@ struct FwdArgs {
   uint32_t q_bytes, k_bytes, v_bytes, o_bytes;  // one head's addressable span, in bytes
   float scale_log2;      // softmax_scale * log2(e)   (times dq * dk for fp8)
   float out_scale;       // 1, or dv for fp8
+  // Packed variable-length batch (null for the dense [B, N, H, D] layout): sequence b is query
+  // rows cu_q[b] .. cu_q[b+1]-1 of [total_q, Hq, D] and key rows cu_k[b] .. cu_k[b+1]-1 of
+  // [total_k, Hkv, D]; the *_b strides are unused, Nq is the longest query sequence, and lse is
+  // [Hq, total_q].
+  const int* cu_q;
+  const int* cu_k;
+  int total_q, total_k;
 };
+
+// One workgroup's sequence: its sizes, the element offsets of its row 0 in q, k, v and out (head
+// offsets not included), the lse index of its row 0 for query head h, and its heads' byte spans.
+struct SeqView {
+  int Nq, Nk;
+  int64_t q0, k0, v0, o0, lse0;
+  uint32_t q_bytes, k_bytes, v_bytes, o_bytes;
+};
+
+// es / oes: bytes per element of the inputs / of out. Offsets read from the device are clamped
+// into [0, total], so every access stays inside the packed tensors whatever they hold.
+__device__ inline SeqView seq_view(const FwdArgs& a, int b, int h, int D, int es, int oes) {
+  SeqView s;
+  if (a.cu_q == nullptr) {
+    s.Nq = a.Nq;
+    s.Nk = a.Nk;
+    s.q0 = b * a.q_b;
+    s.k0 = b * a.k_b;
+    s.v0 = b * a.v_b;
+    s.o0 = b * a.o_b;
+    s.lse0 = ((int64_t)b * a.Hq + h) * a.Nq;
+    s.q_bytes = a.q_bytes;
+    s.k_bytes = a.k_bytes;
+    s.v_bytes = a.v_bytes;
+    s.o_bytes = a.o_bytes;
+    return s;
+  }
+  auto clampi = [](int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); };
+  const int qs = clampi(a.cu_q[b], 0, a.total_q), qe = clampi(a.cu_q[b + 1], qs, a.total_q);
+  const int ks = clampi(a.cu_k[b], 0, a.total_k), ke = clampi(a.cu_k[b + 1], ks, a.total_k);
+  s.Nq = qe - qs;
+  s.Nk = ke - ks;
+  s.q0 = qs * a.q_n;
+  s.k0 = ks * a.k_n;
+  s.v0 = ks * a.v_n;
+  s.o0 = qs * a.o_n;
+  s.lse0 = (int64_t)h * a.total_q + qs;
+  auto span = [&](int n, int64_t row, int e) { return n > 0 ? (uint32_t)(((n - 1) * row + D) * e) : 0u; };
+  s.q_bytes = span(s.Nq, a.q_n, es);
+  s.k_bytes = span(s.Nk, a.k_n, es);
+  s.v_bytes = span(s.Nk, a.v_n, es);
+  s.o_bytes = span(s.Nq, a.o_n, oes);
+  return s;
+}
 
 // Backward pass: one launch of each of three kernels (delta, dq, dk/dv).
 struct BwdArgs {

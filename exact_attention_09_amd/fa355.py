@@ -20,7 +20,7 @@ _DTYPE_CODE = {torch.float16: FA_F16, torch.bfloat16: FA_BF16, torch.float8_e4m3
 _OUT_DTYPE = {FA_F16: torch.float16, FA_BF16: torch.bfloat16, FA_FP8_E4M3: torch.bfloat16}
 
 # Every symbol include/fa355.h declares.
-EXPORTED = ("fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str", "fa_fwd_plan", "fa_kv_tile_range", "fa_version")
+EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str", "fa_fwd_plan", "fa_kv_tile_range", "fa_version")
 
 
 class FaStrides(ctypes.Structure):
@@ -30,6 +30,10 @@ class FaStrides(ctypes.Structure):
 
 class FaBwdStrides(ctypes.Structure):
     _fields_ = [(f"{t}_{a}", ctypes.c_int64) for t in ("q", "k", "v", "o", "do", "dq", "dk", "dv") for a in "bnh"]
+
+
+class FaVarlenStrides(ctypes.Structure):
+    _fields_ = [(f"{t}_{a}", ctypes.c_int64) for t in ("q", "k", "v", "o") for a in "nh"]
 
 
 class FaPlanInfo(ctypes.Structure):
@@ -60,6 +64,9 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                            c_int, c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(FaStrides),
                            c_float, c_int, c_int, c_int, c_int, c_void_p, ctypes.POINTER(c_float)]
+    lib.fa_fwd_varlen.restype = c_int
+    lib.fa_fwd_varlen.argtypes = [c_void_p] * 7 + [c_int] * 7 + [ctypes.POINTER(FaVarlenStrides), c_float, c_int, c_int,
+                                                                  c_int, c_int, c_void_p, ctypes.POINTER(c_float)]
     lib.fa_bwd.restype = c_int
     lib.fa_bwd.argtypes = [c_void_p] * 10 + [ctypes.c_size_t] + [c_int] * 6 + [ctypes.POINTER(FaBwdStrides), c_float,
                                                                    c_int, c_int, c_int, c_int, c_void_p]
@@ -135,6 +142,60 @@ def fwd(q, k, v, causal=False, window=(-1, -1), softmax_scale=None, descale=None
     if lse is None and return_lse:
         lse = torch.empty(B, Hq, Nq, dtype=torch.float32, device=q.device)
     status = fwd_raw(q, k, v, out, lse, causal, window, softmax_scale, descale)
+    if status != 0:
+        raise FaError(status, status_str(status))
+    return out, lse
+
+
+def fwd_varlen_raw(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal=False, window=(-1, -1),
+                   softmax_scale=None, descale=None, stream=None) -> int:
+    """Call fa_fwd_varlen on caller-provided tensors; returns the status code without raising."""
+    lib = load()
+    code = _DTYPE_CODE.get(q.dtype)
+    if code is None:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    total_q, Hq, D = q.shape
+    total_k, Hkv = k.shape[0], k.shape[1]
+    B = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != B + 1 or cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise ValueError("cu_seqlens_q / cu_seqlens_k must be int32 tensors of B + 1 offsets")
+    scale = float(D) ** -0.5 if softmax_scale is None else float(softmax_scale)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    desc = None
+    if descale is not None:
+        desc = (ctypes.c_float * 3)(*[float(x) for x in descale])
+    st = FaVarlenStrides()
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", out)):
+        if t.stride(2) != 1:
+            raise ValueError(f"{name}: the head dimension must be contiguous (stride 1), got {t.stride()}")
+        setattr(st, name + "_n", t.stride(0))
+        setattr(st, name + "_h", t.stride(1))
+    return lib.fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr() if lse is not None else None, cu_seqlens_q.data_ptr(),
+                             cu_seqlens_k.data_ptr(), B, total_q, total_k, int(max_seqlen_q), Hq, Hkv, D,
+                             ctypes.byref(st), scale, int(bool(causal)), int(window[0]), int(window[1]), code, stream,
+                             desc)
+
+
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal=False, window=(-1, -1),
+               softmax_scale=None, descale=None, return_lse=True):
+    """FlashAttention forward over a packed batch of variable-length sequences.
+
+    q: [total_q, Hq, D]; k, v: [total_k, Hkv, D]; cu_seqlens_q / cu_seqlens_k: device int32
+    [B + 1] offsets; max_seqlen_q: the longest query sequence (a host int).
+    Returns (out [total_q, Hq, D], lse [Hq, total_q] fp32 or None).
+    """
+    if not all(t.is_cuda for t in (q, k, v, cu_seqlens_q, cu_seqlens_k)):
+        raise ValueError("all tensors must be device tensors")
+    code = _DTYPE_CODE.get(q.dtype)
+    if code is None or not (q.dtype == k.dtype == v.dtype):
+        raise TypeError(f"unsupported or mixed dtypes {q.dtype} {k.dtype} {v.dtype}")
+    total_q, Hq, D = q.shape
+    out = torch.empty(total_q, Hq, D, dtype=_OUT_DTYPE[code], device=q.device)
+    lse = torch.empty(Hq, total_q, dtype=torch.float32, device=q.device) if return_lse else None
+    status = fwd_varlen_raw(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal, window,
+                            softmax_scale, descale)
     if status != 0:
         raise FaError(status, status_str(status))
     return out, lse

@@ -94,3 +94,56 @@ def make_inputs(w: Workload, seed: int):
     """(q, k, v, descale) for workload ``w`` on the CPU, in storage format."""
     q, k, v = draw_qkv(w.B, w.Nq, w.Nk, w.Hq, w.Hkv, w.D, seed)
     return to_storage(q, k, v, w.dtype)
+
+
+# ---- packed variable-length batches
+@dataclass(frozen=True)
+class VarlenWorkload:
+    """B sequences with seeded lengths, uniform on [len_lo, len_hi] (queries and keys of a
+    sequence have the same length), packed along the token axis."""
+    name: str
+    B: int
+    len_lo: int
+    len_hi: int
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: str
+    causal: bool = False
+    window: tuple = (-1, -1)
+    scale: float | None = None
+
+    def softmax_scale(self) -> float:
+        return self.scale if self.scale is not None else self.D ** -0.5
+
+    def lengths(self, seed: int = 0):
+        g = torch.Generator().manual_seed(10_000 + seed)
+        return torch.randint(self.len_lo, self.len_hi + 1, (self.B,), generator=g).tolist()
+
+
+def offsets(lengths):
+    """int32 [B + 1] cumulative offsets of the sequence lengths."""
+    out = [0]
+    for n in lengths:
+        out.append(out[-1] + int(n))
+    return torch.tensor(out, dtype=torch.int32)
+
+
+def make_varlen_inputs(lengths_q, lengths_k, Hq, Hkv, D, dtype: str, seed: int):
+    """Packed (q [total_q, Hq, D], k, v [total_k, Hkv, D], cu_q, cu_k, descale) on the CPU, in storage
+    format; the values are one draw_qkv draw of a batch of one packed sequence."""
+    cu_q, cu_k = offsets(lengths_q), offsets(lengths_k)
+    q, k, v = draw_qkv(1, int(cu_q[-1]), int(cu_k[-1]), Hq, Hkv, D, seed)
+    q, k, v, d = to_storage(q[0], k[0], v[0], dtype)
+    return q, k, v, cu_q, cu_k, d
+
+
+# The pages' variable-length use (no padding): a mix of sequence lengths with about as many
+# tokens as the [4, 4096, 32, 64] causal workload.
+VARLEN_WORKLOADS = {
+    w.name: w
+    for w in [
+        VarlenWorkload("varlen_b8_len512to4096_h32_d64_f16", 8, 512, 4096, 32, 32, 64, "f16", causal=True, scale=0.125),
+        VarlenWorkload("varlen_b16_len128to8192_hq32_hkv8_d128_bf16", 16, 128, 8192, 32, 8, 128, "bf16", causal=True),
+    ]
+}

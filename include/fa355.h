@@ -97,6 +97,44 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* out, float* 
                  float softmax_scale, int causal, int window_left, int window_right,
                  fa_dtype dtype, hipStream_t stream, const float* descale_qkv);
 
+/* Element strides of packed variable-length tensors: token and head axes (headdim stride 1). */
+typedef struct fa_varlen_strides {
+  int64_t q_n, q_h;
+  int64_t k_n, k_h;
+  int64_t v_n, v_h;
+  int64_t o_n, o_h;
+} fa_varlen_strides;
+
+/*
+ * fa_fwd_varlen — fa_fwd over a packed batch of B sequences of different lengths, with no
+ * padding. The pages list variable sequence lengths among the ROCm backends' features ("What
+ * FlashAttention is and how it speeds up attention", section "Versions, hardware and sources")
+ * and describe kernels that adapt to dynamic sequence lengths without padding ("FlashAttention
+ * V3 principles and practice", section 1); the interface is this library's reading.
+ *
+ * q                  device [total_q, Hq, D]; k, v: device [total_k, Hkv, D]; out: device
+ *                    [total_q, Hq, D] (dtype rules of fa_fwd); strides in elements, headdim 1.
+ * cu_seqlens_q/_k    device int32 [B + 1]: non-decreasing, from 0 to total_q / total_k. Sequence
+ *                    b is query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows
+ *                    cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1, and is computed exactly as fa_fwd
+ *                    computes one sequence of those lengths (causal alignment and window use its
+ *                    own lengths); a sequence with queries but no keys gives out = 0 and
+ *                    lse = -inf on its rows. The offsets are read on the device (this call does
+ *                    not synchronise); offsets outside [0, total] are clamped, so the kernel never
+ *                    reads or writes outside the packed tensors whatever they hold.
+ * max_seqlen_q       host int, 1 <= max_seqlen_q <= total_q: no sequence has more queries (rows of a
+ *                    longer one past max_seqlen_q are not written).
+ * lse                device fp32 [Hq, total_q] contiguous, or NULL.
+ * Other arguments, validation, ownership, errors and asynchrony as for fa_fwd (total_q, total_k
+ * and max_seqlen_q take the places of Nq and Nk in the size checks).
+ */
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                        int total_q, int total_k, int max_seqlen_q, int Hq, int Hkv, int D,
+                        const fa_varlen_strides* strides, float softmax_scale, int causal,
+                        int window_left, int window_right, fa_dtype dtype, hipStream_t stream,
+                        const float* descale_qkv);
+
 /* Element strides of the backward pass's tensors (headdim stride 1). */
 typedef struct fa_bwd_strides {
   int64_t q_b, q_n, q_h;
