@@ -10,6 +10,9 @@ Metric: attention forward TFLOP/s with FLOPs = 4 * B * Hq * Nq * Nk * D, halved 
 a sliding window the admitted-pair count replaces Nq * Nk (4 * B * Hq * D * pairs). Inputs are
 resident in device memory before the timed region. Prints one JSON line.
 
+``--workload varlen_...`` times fa_fwd_varlen on a packed batch of sequences of seeded lengths
+(no padding); its FLOPs are the sum of the sequences' own (causal halved).
+
 ``--pass bwd`` times the backward pass (fa_bwd: dq, dk, dv for a seeded N(0, 1) upstream gradient,
 after one forward pass that provides out and lse) on the same workload; its FLOPs are counted as
 2.5 times the forward's (the five products of the method's backward pass).
@@ -68,6 +71,18 @@ def metric_flops(w):
     return 4.0 * w.B * w.Hq * w.D * admitted_pairs(w.Nq, w.Nk, w.causal, w.window)
 
 
+def varlen_flops(w, lengths):
+    """Metric FLOPs of one fa_fwd_varlen call: the sum over the sequences (queries = keys)."""
+    total = 0.0
+    for n in lengths:
+        if w.window == (-1, -1):
+            f = 4.0 * w.Hq * n * n * w.D
+            total += f / 2 if w.causal else f
+        else:
+            total += 4.0 * w.Hq * w.D * admitted_pairs(n, n, w.causal, w.window)
+    return total
+
+
 def algorithmic_bytes(w):
     """Bytes the pass must move at least: q, k, v read once, out and lse written once."""
     es = 1 if w.dtype == "e4m3" else 2
@@ -103,6 +118,18 @@ def committed_traffic(workload):
     return t.get("hbm_bytes_per_launch")
 
 
+def blas_threads():
+    """(threads, name) of the BLAS the oracle's matrix products run on."""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max((i.get("num_threads", 1) for i in blas), default=1)
+        name = ",".join(sorted({i.get("internal_api", "?") for i in blas})) or "unknown"
+        return int(threads), name
+    except Exception:  # pragma: no cover
+        return 1, "unknown"
+
+
 def cpu_baseline(w, q, k, v, descale, budget_s, dout=None):
     """Time the fp64 oracle on whole heads of the same inputs until budget_s has passed (the
     gradient oracle when dout is given)."""
@@ -119,13 +146,7 @@ def cpu_baseline(w, q, k, v, descale, budget_s, dout=None):
             return decode_bf16_bits(x.view(torch.int16).numpy().view(np.uint16))
         return decode_e4m3_codes(x.view(torch.uint8).numpy(), s)
 
-    try:
-        from threadpoolctl import threadpool_info
-        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
-        threads = max((i.get("num_threads", 1) for i in blas), default=1)
-        blas_name = ",".join(sorted({i.get("internal_api", "?") for i in blas})) or "unknown"
-    except Exception:  # pragma: no cover
-        threads, blas_name = 1, "unknown"
+    threads, blas_name = blas_threads()
     dq, dk, dv = descale if descale is not None else (1.0, 1.0, 1.0)
     G = w.Hq // w.Hkv
     heads = 0
@@ -186,7 +207,7 @@ def main():
     import torch
 
     import exact_attention_09_amd as fa
-    from exact_attention_09_amd.inputs import WORKLOADS, make_inputs
+    from exact_attention_09_amd.inputs import VARLEN_WORKLOADS, WORKLOADS, make_inputs
 
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
@@ -205,6 +226,11 @@ def main():
                           "launches": args.warmup + args.steps}))
         return
 
+    if args.workload in VARLEN_WORKLOADS:
+        if args.pass_ == "bwd":
+            print(json.dumps({"error": "the backward pass takes dense [B, N, H, D] batches"}))
+            sys.exit(2)
+        return bench_varlen(args, VARLEN_WORKLOADS[args.workload], dev)
     w = WORKLOADS[args.workload]
     seed = w.seeds[0]
     q, k, v, descale = make_inputs(w, seed)
@@ -315,6 +341,107 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v, descale, args.cpu_baseline_seconds,
                                            dout if bwd else None)
     print(json.dumps(rec), flush=True)
+
+
+def timed(step, args, stream):
+    """Warm-up, then args.steps launches bracketed by HIP events on the launch stream; returns
+    (ms_per_step by wall clock, mean launch s, median launch s)."""
+    import torch
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall / args.steps * 1e3, sum(ms) / len(ms) / 1e3, sorted(ms)[len(ms) // 2] / 1e3
+
+
+def bench_varlen(args, w, dev):
+    """fa_fwd_varlen on the packed workload w (queries = keys per sequence)."""
+    import torch
+
+    import exact_attention_09_amd as fa
+    from exact_attention_09_amd.inputs import make_varlen_inputs
+
+    lengths = w.lengths(0)
+    q, k, v, cu_q, cu_k, descale = make_varlen_inputs(lengths, lengths, w.Hq, w.Hkv, w.D, w.dtype, seed=0)
+    qd, kd, vd, cqd, ckd = q.to(dev), k.to(dev), v.to(dev), cu_q.to(dev), cu_k.to(dev)
+    total = int(cu_q[-1])
+    out = torch.empty(total, w.Hq, w.D, dtype=torch.float16 if w.dtype == "f16" else torch.bfloat16, device=dev)
+    lse = torch.empty(w.Hq, total, dtype=torch.float32, device=dev)
+    scale = w.softmax_scale()
+
+    def step():
+        st = fa.fwd_varlen_raw(qd, kd, vd, out, lse, cqd, ckd, max(lengths), w.causal, w.window, scale, descale)
+        if st != 0:
+            raise fa.FaError(st, fa.status_str(st))
+
+    ms_per_step, avg_s, med_s = timed(step, args, torch.cuda.current_stream(dev))
+    flops = varlen_flops(w, lengths)
+    peak = PEAK_TFLOPS[w.dtype]
+    es = 1 if w.dtype == "e4m3" else 2
+    alg_bytes = total * w.Hq * w.D * es + 2 * total * w.Hkv * w.D * es + total * w.Hq * w.D * 2 + total * w.Hq * 4
+    rec = {
+        "metric": METRIC, "value": round(flops / (ms_per_step / 1e3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "sequences": w.B, "lengths": lengths, "total_tokens": total, "Hq": w.Hq,
+                   "Hkv": w.Hkv, "D": w.D, "causal": w.causal, "window": list(w.window), "softmax_scale": scale,
+                   "metric_flops": flops},
+        "pct_of_mfma_peak": round(100.0 * flops / (ms_per_step / 1e3) / 1e12 / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(flops / avg_s / 1e12, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(flops / avg_s / 1e12 / peak, 4), "traffic": committed_traffic(w.name),
+                     "kernel_avg_us": round(avg_s * 1e6, 3), "kernel_median_us": round(med_s * 1e6, 3),
+                     "algorithmic_bytes": alg_bytes, "algorithmic_GBps": round(alg_bytes / avg_s / 1e9, 1)},
+    }
+    if args.cpu_baseline_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline_varlen(w, lengths, q, k, v, cu_q, descale, args.cpu_baseline_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline_varlen(w, lengths, q, k, v, cu_q, descale, budget_s):
+    """The varlen oracle on whole (sequence, head) pairs until budget_s has passed."""
+    import numpy as np
+    import torch
+
+    from oracle import attention_varlen_fp64, decode_bf16_bits, decode_f16_bits
+
+    def dec(x):
+        x = x.contiguous()
+        if x.dtype == torch.float16:
+            return decode_f16_bits(x.view(torch.int16).numpy().view(np.uint16))
+        return decode_bf16_bits(x.view(torch.int16).numpy().view(np.uint16))
+
+    G = w.Hq // w.Hkv
+    done_flops, n_pairs = 0.0, 0
+    t0 = time.perf_counter()
+    elapsed = 0.0
+    for b, n in enumerate(lengths):
+        s = int(cu_q[b])
+        for h in range(w.Hq):
+            g = h // G
+            attention_varlen_fp64(dec(q[s:s + n, h:h + 1]), dec(k[s:s + n, g:g + 1]), dec(v[s:s + n, g:g + 1]),
+                                  [0, n], [0, n], w.softmax_scale(), w.causal, w.window)
+            done_flops += varlen_flops(w, [n]) / w.Hq
+            n_pairs += 1
+            elapsed = time.perf_counter() - t0
+            if elapsed >= budget_s:
+                break
+        if elapsed >= budget_s:
+            break
+    threads, blas_name = blas_threads()
+    return {"value": done_flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_pairs} of {len(lengths) * w.Hq} (sequence, head) pairs of the same inputs, full fp64 "
+                      f"score matrix per pair, {elapsed:.1f} s wall; metric FLOPs of those pairs / wall time; "
+                      f"BLAS={blas_name} threads={threads}, host logical CPUs={os.cpu_count()}"}
 
 
 if __name__ == "__main__":

@@ -56,12 +56,19 @@ __device__ inline int xcd_remap(int id, int n) {
 //    under 4-way GQA), longest tiles of the chunk first: the chunk in flight keeps the XCD's L2
 //    working set small, every XCD gets the same mix of long and short tiles, and the longest
 //    work starts first, which keeps the launch's tail short.
-//  * Causal otherwise: longest tiles of every head first, consecutive ids on different XCDs.
-__device__ inline void schedule_block(int id, int n, int num_tiles, int H, bool causal, int* b, int* h, int* t) {
+//  * Causal otherwise, and packed batches of sequences of different lengths (`spread`: whole
+//    sequences on one XCD would leave the XCDs unequally loaded): highest tiles of every head
+//    first, consecutive ids on different XCDs.
+__device__ inline void schedule_block(int id, int n, int num_tiles, int H, bool causal, int* b, int* h, int* t,
+                                      bool spread = false) {
   constexpr int kChunk = 4;
   const int n_bh = n / num_tiles;
   int bh;
-  if (!causal) {
+  if (spread) {
+    const int rank = id / n_bh;
+    bh = id - rank * n_bh;
+    *t = num_tiles - 1 - rank;
+  } else if (!causal) {
     const int L = xcd_remap(id, n);
     bh = L / num_tiles;
     *t = L - bh * num_tiles;

@@ -70,7 +70,7 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
 
   // ---- which (batch, head, query tile) this workgroup computes
   int b, h, qt;
-  schedule_block(blockIdx.x, gridDim.x, a.num_q_tiles, a.Hq, a.causal != 0, &b, &h, &qt);
+  schedule_block(blockIdx.x, gridDim.x, a.num_q_tiles, a.Hq, a.causal != 0, &b, &h, &qt, a.cu_q != nullptr);
   const int hk = h / a.group;                    // MQA/GQA: K/V head of this query head
   const int q0 = qt * BM;
   const SeqView sv = seq_view(a, b, h, D, ES, ES);
