@@ -22,6 +22,8 @@ Contents:
     respect to q, k and v for an upstream gradient of the output (the backward pass).
   * :mod:`oracle.varlen` — ``attention_varlen_fp64``: the same definition applied to each
     sequence of a packed variable-length batch.
+  * :mod:`oracle.kvcache` — ``attention_kvcache_fp64``: queries against each sequence's keys in
+    a dense or paged key/value cache (the decode-shaped workload).
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against closed forms, invariants,
 the worked example, brute force and an independent library routine.
@@ -29,12 +31,15 @@ the worked example, brute force and an independent library routine.
 from .attention import admitted, attention_fp64, attention_rows_fp64, kv_head_of, tiled_online_fp64
 from .backward import attention_bwd_fp64
 from .formats import decode_bf16_bits, decode_e4m3_codes, decode_f16_bits, e4m3_table
+from .kvcache import attention_kvcache_fp64, gather_kv
 from .varlen import attention_varlen_fp64
 
 __all__ = [
     "admitted",
     "attention_bwd_fp64",
     "attention_fp64",
+    "attention_kvcache_fp64",
+    "gather_kv",
     "attention_rows_fp64",
     "attention_varlen_fp64",
     "kv_head_of",
