@@ -44,10 +44,14 @@ DEFAULT_WORKLOAD = "causal_b4_h32_n4096_d64_f16"
 METRIC = "attention fwd TFLOP/s (4·B·H·Nq·Nk·D, causal halved) and % of MFMA peak"
 METRIC_BWD = "attention bwd TFLOP/s (2.5 x the forward FLOPs: five products of the forward's size)"
 BWD_FLOP_FACTOR = 2.5
-KERNEL_SOURCES = ["exact_attention_09_amd/csrc/fa_fwd_f16.hip", "exact_attention_09_amd/csrc/fa_f16_common.hpp",
-                  "exact_attention_09_amd/csrc/fa_fwd_fp8.hip", "exact_attention_09_amd/csrc/fa_device.hpp",
-                  "exact_attention_09_amd/csrc/fa_mask.hpp", "exact_attention_09_amd/csrc/fa_kernels.hpp",
-                  "exact_attention_09_amd/csrc/fa355_api.hip"]
+_CSRC = "exact_attention_09_amd/csrc/"
+_SHARED = ["fa_f16_common.hpp", "fa_device.hpp", "fa_mask.hpp", "fa_kernels.hpp", "fa355_api.hip"]
+# sources whose change makes a committed counter summary stale, per pass
+KERNEL_SOURCES = {
+    "fwd": [_CSRC + f for f in ["fa_fwd_f16.hip", "fa_fwd_fp8.hip"] + _SHARED],
+    "bwd": [_CSRC + f for f in ["fa_fwd_f16.hip", "fa_bwd_f16.hip", "fa_tile.hpp"] + _SHARED],
+    "decode": [_CSRC + f for f in ["fa_decode.hip", "fa_tile.hpp"] + _SHARED],
+}
 
 
 def admitted_pairs(Nq, Nk, causal, window):
@@ -98,22 +102,22 @@ def algorithmic_bytes_bwd(w):
     return (4 * rows_q * w.D * es + 4 * w.B * w.Nk * w.Hkv * w.D * es + rows_q * 4 + 4 * rows_q * 4)
 
 
-def kernel_source_hash():
+def kernel_source_hash(pass_="fwd"):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES[pass_]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def committed_traffic(workload):
+def committed_traffic(workload, pass_="fwd"):
     """HBM bytes per launch from the committed counter summary, if taken on this kernel source."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash(pass_):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -306,7 +310,7 @@ def main():
     value = flops / (ms_per_step / 1e3) / 1e12
     achieved = flops / avg_kernel_s / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = committed_traffic(("bwd_" if bwd else "") + w.name)
+    traffic = committed_traffic(("bwd_" if bwd else "") + w.name, "bwd" if bwd else "fwd")
     alg_bytes = algorithmic_bytes_bwd(w) if bwd else algorithmic_bytes(w)
 
     rec = {

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa355.so")
 OBJ = os.path.join(PKG, "_build")
 
-SOURCES = ["fa355_api.hip", "fa_fwd_f16.hip", "fa_fwd_fp8.hip", "fa_bwd_f16.hip"]
+SOURCES = ["fa355_api.hip", "fa_fwd_f16.hip", "fa_fwd_fp8.hip", "fa_bwd_f16.hip", "fa_decode.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -95,6 +95,43 @@ int64_t bwd_workspace_floats(int B, int Nq, int Nk, int Hq, int Hkv, int D) {
 
 }  // namespace
 
+namespace {
+
+// Key splits of fa_fwd_kvcache: enough waves to cover the chip several times over (one wave per
+// (batch, K/V head, row block, split)), splits of at least kDecMinKeys keys, a multiple of 32.
+constexpr int64_t kDecTargetWaves = 4096;
+constexpr int kDecMinKeys = 256;
+void dec_split(int B, int Hkv, int row_blocks, int max_seqlen_k, int* n_split, int* split_keys) {
+  const int64_t base = (int64_t)B * Hkv * row_blocks;
+  const int64_t want = (kDecTargetWaves + base - 1) / base;
+  int64_t keys = ((int64_t)max_seqlen_k + want - 1) / want;
+  keys = keys < kDecMinKeys ? kDecMinKeys : (keys + 31) / 32 * 32;
+  *split_keys = (int)keys;
+  *n_split = (int)(((int64_t)max_seqlen_k + keys - 1) / keys);
+}
+
+int64_t dec_workspace_floats(int B, int Nq, int Hq, int Hkv, int D, int max_seqlen_k) {
+  const int row_blocks = ((Hq / Hkv) * Nq + 31) / 32;
+  int ns, sk;
+  dec_split(B, Hkv, row_blocks, max_seqlen_k, &ns, &sk);
+  return ns > 1 ? (int64_t)ns * B * Hq * Nq * (D + 1) : 0;
+}
+
+fa_status check_kvcache_sizes(int B, int Nq, int Hq, int Hkv, int D, int max_seqlen_k) {
+  if (B < 1 || Nq < 1 || Hq < 1 || Hkv < 1 || max_seqlen_k < 1) return FA_ERR_SHAPE;
+  if (Nq > kMaxSeq || max_seqlen_k > kMaxSeq || Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if ((int64_t)(Hq / Hkv) * Nq > kMaxSeq) return FA_ERR_SHAPE;
+  if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+  const int64_t row_blocks = ((int64_t)(Hq / Hkv) * Nq + 31) / 32;
+  int ns, sk;
+  dec_split(B, Hkv, (int)(row_blocks < kMaxSeq ? row_blocks : kMaxSeq), max_seqlen_k, &ns, &sk);
+  if ((int64_t)B * Hkv * row_blocks * ns >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+  if ((int64_t)B * Hq * Nq * (D / 8) >= ((int64_t)1 << 40)) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int fa_version(void) { return 100; }
@@ -288,6 +325,57 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, 
   a.num_q_tiles = (max_seqlen_q + ts.block_m - 1) / ts.block_m;
   const int64_t grid = (int64_t)B * Hq * a.num_q_tiles;
   const hipError_t e = fa::launch_fwd(a, D, dtype, grid, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t fa_fwd_kvcache_workspace_bytes(int B, int Nq, int Hq, int Hkv, int D, int max_seqlen_k) {
+  if (check_kvcache_sizes(B, Nq, Hq, Hkv, D, max_seqlen_k) != FA_OK) return 0;
+  return (size_t)dec_workspace_floats(B, Nq, Hq, Hkv, D, max_seqlen_k) * 4u;
+}
+
+fa_status fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                         const int32_t* seqlens_k, const int32_t* block_table, int B, int Nq, int Hq, int Hkv, int D,
+                         int max_seqlen_k, int page_size, int max_pages_per_seq, int num_pages, const fa_strides* s,
+                         float softmax_scale, int causal, int window_left, int window_right, fa_dtype dtype,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k_cache || !v_cache || !out || !seqlens_k || !s) return FA_ERR_NULL;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  fa_status st = check_kvcache_sizes(B, Nq, Hq, Hkv, D, max_seqlen_k);
+  if (st != FA_OK) return st;
+  if (block_table != nullptr && (page_size < 1 || max_pages_per_seq < 1 || num_pages < 1)) return FA_ERR_SHAPE;
+  if (window_left < -1 || window_right < -1) return FA_ERR_WINDOW;
+  if (!finite_pos(softmax_scale)) return FA_ERR_SCALE;
+  const int64_t need = dec_workspace_floats(B, Nq, Hq, Hkv, D, max_seqlen_k) * 4;
+  if ((uint64_t)workspace_bytes < (uint64_t)need || (need > 0 && workspace == nullptr)) return FA_ERR_WORKSPACE;
+  const int64_t str[12] = {s->q_b, s->q_n, s->q_h, s->k_b, s->k_n, s->k_h, s->v_b, s->v_n, s->v_h, s->o_b, s->o_n, s->o_h};
+  for (int i = 0; i < 12; ++i)
+    if (str[i] < 0 || (str[i] * 2) % 16 != 0) return FA_ERR_STRIDES;
+  if ((Nq > 1 && s->o_n < D) || (Hq > 1 && s->o_h < D) || (B > 1 && s->o_b < D)) return FA_ERR_STRIDES;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(workspace) ||
+      ((uintptr_t)lse & 3u) || ((uintptr_t)seqlens_k & 3u) || ((uintptr_t)block_table & 3u))
+    return FA_ERR_STRIDES;
+
+  fa::DecArgs a;
+  a.q = q; a.kc = k_cache; a.vc = v_cache; a.o = out; a.lse = lse;
+  a.seqlens_k = seqlens_k;
+  a.block_table = block_table;
+  a.part = (float*)workspace;
+  a.B = B; a.Nq = Nq; a.Hq = Hq; a.Hkv = Hkv; a.group = Hq / Hkv;
+  a.max_seqlen_k = max_seqlen_k;
+  a.page_size = block_table ? page_size : 0;
+  a.max_pages = block_table ? max_pages_per_seq : 0;
+  a.num_pages = block_table ? num_pages : 0;
+  a.causal = causal ? 1 : 0;
+  a.wl = window_left;
+  a.wr = window_right;
+  a.row_blocks = (a.group * Nq + 31) / 32;
+  dec_split(B, Hkv, a.row_blocks, max_seqlen_k, &a.n_split, &a.split_keys);
+  a.q_b = s->q_b; a.q_n = s->q_n; a.q_h = s->q_h;
+  a.k_b = s->k_b; a.k_n = s->k_n; a.k_h = s->k_h;
+  a.v_b = s->v_b; a.v_n = s->v_n; a.v_h = s->v_h;
+  a.o_b = s->o_b; a.o_n = s->o_n; a.o_h = s->o_h;
+  a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  const hipError_t e = fa::launch_decode(a, D, dtype, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

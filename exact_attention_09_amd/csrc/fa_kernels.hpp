@@ -102,6 +102,26 @@ struct BwdArgs {
   float scale_log2;      // softmax_scale * log2(e)
 };
 
+// Queries against a dense or paged key/value cache (decode-shaped: few queries, long keys), split
+// over the keys; one wave per workgroup.
+struct DecArgs {
+  const void* q;             // [B, Nq, Hq, D]
+  const void* kc;            // dense [B, max_seqlen_k, Hkv, D], or paged [num_pages, page_size, Hkv, D]
+  const void* vc;
+  void* o;                   // [B, Nq, Hq, D]
+  float* lse;                // [B, Hq, Nq] or null
+  const int* seqlens_k;      // [B]
+  const int* block_table;    // [B, max_pages] page ids, or null for a dense cache
+  float* part;               // n_split > 1: fp32 outputs [n_split, B * Hq * Nq, D], then lse [n_split, B * Hq * Nq]
+  int B, Nq, Hq, Hkv, group, max_seqlen_k, page_size, max_pages, num_pages;
+  int causal, wl, wr;
+  int row_blocks;            // ceil(group * Nq / 32): the group's query rows, 32 per wave
+  int n_split, split_keys;   // splits per (batch, K/V head, row block); keys per split (a multiple of 32)
+  int64_t q_b, q_n, q_h, k_b, k_n, k_h, v_b, v_n, v_h, o_b, o_n, o_h;   // k_b, v_b: page stride when paged
+  float scale_log2;
+};
+hipError_t launch_decode(const DecArgs& a, int D, int dtype, hipStream_t stream);
+
 constexpr int kBwdQRows = 128;   // query rows per dq workgroup
 constexpr int kBwdKRows = 128;   // keys per dk/dv workgroup
 hipError_t launch_bwd(const BwdArgs& a, int D, int dtype, hipStream_t stream);

@@ -20,7 +20,7 @@ _DTYPE_CODE = {torch.float16: FA_F16, torch.bfloat16: FA_BF16, torch.float8_e4m3
 _OUT_DTYPE = {FA_F16: torch.float16, FA_BF16: torch.bfloat16, FA_FP8_E4M3: torch.bfloat16}
 
 # Every symbol include/fa355.h declares.
-EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str", "fa_fwd_plan", "fa_kv_tile_range", "fa_version")
+EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str", "fa_fwd_plan", "fa_kv_tile_range", "fa_version")
 
 
 class FaStrides(ctypes.Structure):
@@ -67,6 +67,11 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_varlen.restype = c_int
     lib.fa_fwd_varlen.argtypes = [c_void_p] * 7 + [c_int] * 7 + [ctypes.POINTER(FaVarlenStrides), c_float, c_int, c_int,
                                                                   c_int, c_int, c_void_p, ctypes.POINTER(c_float)]
+    lib.fa_fwd_kvcache.restype = c_int
+    lib.fa_fwd_kvcache.argtypes = ([c_void_p] * 7 + [c_int] * 9 + [ctypes.POINTER(FaStrides), c_float, c_int, c_int,
+                                   c_int, c_int, c_void_p, ctypes.c_size_t, c_void_p])
+    lib.fa_fwd_kvcache_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_fwd_kvcache_workspace_bytes.argtypes = [c_int] * 6
     lib.fa_bwd.restype = c_int
     lib.fa_bwd.argtypes = [c_void_p] * 10 + [ctypes.c_size_t] + [c_int] * 6 + [ctypes.POINTER(FaBwdStrides), c_float,
                                                                    c_int, c_int, c_int, c_int, c_void_p]
@@ -196,6 +201,64 @@ def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal=False, 
     lse = torch.empty(Hq, total_q, dtype=torch.float32, device=q.device) if return_lse else None
     status = fwd_varlen_raw(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal, window,
                             softmax_scale, descale)
+    if status != 0:
+        raise FaError(status, status_str(status))
+    return out, lse
+
+
+def kvcache_workspace(q, Hkv, max_seqlen_k):
+    """The device workspace fa_fwd_kvcache needs for queries q [B, Nq, Hq, D] (None when none)."""
+    B, Nq, Hq, D = q.shape
+    nbytes = load().fa_fwd_kvcache_workspace_bytes(B, Nq, Hq, Hkv, D, int(max_seqlen_k))
+    return torch.empty(nbytes // 4, dtype=torch.float32, device=q.device) if nbytes else None
+
+
+def fwd_kvcache_raw(q, k_cache, v_cache, out, lse, seqlens_k, block_table, max_seqlen_k, num_pages=0,
+                    causal=False, window=(-1, -1), softmax_scale=None, workspace=None, stream=None) -> int:
+    """Call fa_fwd_kvcache on caller-provided tensors; returns the status code without raising.
+    Dense cache: block_table None, k_cache/v_cache [B, max_seqlen_k, Hkv, D]. Paged: k_cache/v_cache
+    [num_pages, page_size, Hkv, D] and block_table int32 [B, max_pages_per_seq]."""
+    lib = load()
+    code = _DTYPE_CODE.get(q.dtype)
+    if code is None or code == FA_FP8_E4M3:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    B, Nq, Hq, D = q.shape
+    Hkv = k_cache.shape[2]
+    scale = float(D) ** -0.5 if softmax_scale is None else float(softmax_scale)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    page_size = k_cache.shape[1] if block_table is not None else 0
+    max_pages = block_table.shape[1] if block_table is not None else 0
+    npages = (num_pages or k_cache.shape[0]) if block_table is not None else 0
+    st = _strides(q, k_cache, v_cache, out)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return lib.fa_fwd_kvcache(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
+                              lse.data_ptr() if lse is not None else None, seqlens_k.data_ptr(),
+                              block_table.data_ptr() if block_table is not None else None, B, Nq, Hq, Hkv, D,
+                              int(max_seqlen_k), page_size, max_pages, npages, ctypes.byref(st), scale,
+                              int(bool(causal)), int(window[0]), int(window[1]), code,
+                              workspace.data_ptr() if workspace is not None else None, ws_bytes, stream)
+
+
+def fwd_kvcache(q, k_cache, v_cache, seqlens_k, block_table=None, max_seqlen_k=None, causal=False,
+                window=(-1, -1), softmax_scale=None):
+    """Attention of q [B, Nq, Hq, D] against each sequence's keys in a dense or paged cache.
+    ``seqlens_k``: device int32 [B]; ``max_seqlen_k``: host bound on them (default: the cache's
+    capacity). Returns (out [B, Nq, Hq, D], lse [B, Hq, Nq] fp32)."""
+    if not all(t.is_cuda for t in (q, k_cache, v_cache, seqlens_k)):
+        raise ValueError("all tensors must be device tensors")
+    if block_table is not None and (not block_table.is_cuda or block_table.dtype != torch.int32):
+        raise ValueError("block_table must be a device int32 tensor")
+    if seqlens_k.dtype != torch.int32:
+        raise ValueError("seqlens_k must be int32")
+    B, Nq, Hq, D = q.shape
+    if max_seqlen_k is None:
+        max_seqlen_k = block_table.shape[1] * k_cache.shape[1] if block_table is not None else k_cache.shape[1]
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Hq, Nq, dtype=torch.float32, device=q.device)
+    ws = kvcache_workspace(q, k_cache.shape[2], max_seqlen_k)
+    status = fwd_kvcache_raw(q, k_cache, v_cache, out, lse, seqlens_k, block_table, max_seqlen_k, causal=causal,
+                             window=window, softmax_scale=softmax_scale, workspace=ws)
     if status != 0:
         raise FaError(status, status_str(status))
     return out, lse

@@ -147,3 +147,81 @@ VARLEN_WORKLOADS = {
         VarlenWorkload("varlen_b16_len128to8192_hq32_hkv8_d128_bf16", 16, 128, 8192, 32, 8, 128, "bf16", causal=True),
     ]
 }
+
+
+# ---- decode-shaped attention against a (paged) key/value cache
+@dataclass(frozen=True)
+class KVCacheWorkload:
+    """B sequences, Nq new queries each, against cached keys of seeded lengths uniform on
+    [len_lo, len_hi]; page_size 0 means a dense cache [B, len_hi, Hkv, D]."""
+    name: str
+    B: int
+    Nq: int
+    len_lo: int
+    len_hi: int
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: str
+    page_size: int = 0
+    causal: bool = False
+    scale: float | None = None
+
+    def softmax_scale(self) -> float:
+        return self.scale if self.scale is not None else self.D ** -0.5
+
+    def lengths(self, seed: int = 0):
+        g = torch.Generator().manual_seed(20_000 + seed)
+        return torch.randint(self.len_lo, self.len_hi + 1, (self.B,), generator=g).tolist()
+
+
+def _randn_storage(shape, g, dtype: str, chunk_rows: int = 4096):
+    """N(0, 1) fp32 draws rounded to the storage type, generated along the first axis in chunks
+    (so that a multi-GB cache never exists in fp32)."""
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    out = torch.empty(shape, dtype=tdt)
+    for r0 in range(0, shape[0], chunk_rows):
+        r1 = min(shape[0], r0 + chunk_rows)
+        out[r0:r1] = torch.randn((r1 - r0,) + tuple(shape[1:]), generator=g).to(tdt)
+    return out
+
+
+def make_kvcache_inputs(B, Nq, Hq, Hkv, D, dtype: str, lengths, page_size: int, seed: int, max_len: int | None = None):
+    """(q [B, Nq, Hq, D], k_cache, v_cache, seqlens_k int32 [B], block_table int32 [B, pages] or None) on the
+    CPU. Paged: each sequence's pages are a seeded random choice among all pages of the pool
+    (pool = the pages the sequences need plus 3 spare); unused table entries are 0. Dense: the
+    cache is [B, max_len, Hkv, D] (max_len defaults to the longest sequence)."""
+    g = torch.Generator().manual_seed(seed)
+    q = _randn_storage((B, Nq, Hq, D), g, dtype)
+    seqlens = torch.tensor(lengths, dtype=torch.int32)
+    if page_size == 0:
+        L = max_len or max(max(lengths), 1)
+        k = _randn_storage((B, L, Hkv, D), g, dtype)
+        v = _randn_storage((B, L, Hkv, D), g, dtype)
+        return q, k, v, seqlens, None
+    need = [(n + page_size - 1) // page_size for n in lengths]
+    num_pages = sum(need) + 3
+    perm = torch.randperm(num_pages, generator=g)
+    table = torch.zeros(B, max(max(need), 1), dtype=torch.int32)
+    at = 0
+    for b, npg in enumerate(need):
+        table[b, :npg] = perm[at:at + npg].to(torch.int32)
+        at += npg
+    k = _randn_storage((num_pages, page_size, Hkv, D), g, dtype)
+    v = _randn_storage((num_pages, page_size, Hkv, D), g, dtype)
+    return q, k, v, seqlens, table
+
+
+# The pages' serving configuration: 16-token cache pages and up to 128 sequences
+# ("FlashAttention V3 principles and practice", section 4), a Llama-3-8B-shaped attention layer
+# (32 query heads, 8 K/V heads, D = 128, bf16), one new token per sequence; and a dense cache with
+# 4 new tokens per sequence (causal among them).
+KVCACHE_WORKLOADS = {
+    w.name: w
+    for w in [
+        KVCacheWorkload("decode_paged16_b128_len512to8192_hq32_hkv8_d128_bf16", 128, 1, 512, 8192, 32, 8, 128, "bf16",
+                        page_size=16),
+        KVCacheWorkload("decode_dense_b16_nq4_len4096to16384_hq32_hkv8_d128_bf16", 16, 4, 4096, 16384, 32, 8, 128,
+                        "bf16", causal=True),
+    ]
+}

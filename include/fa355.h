@@ -135,6 +135,47 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, 
                         int window_left, int window_right, fa_dtype dtype, hipStream_t stream,
                         const float* descale_qkv);
 
+/*
+ * fa_fwd_kvcache — attention of Nq queries per sequence against each sequence's keys in a dense
+ * or paged key/value cache: the decode-shaped workload (few queries, long keys). The pages name a
+ * paged KV cache ("Flash Attention - Fast Memory-Efficient Attention", skill page, section
+ * "Advanced features"; "FlashAttention V3 principles and practice", section 4, with 16-token
+ * cache blocks) but no interface; this is the library's reading. Sequence b is computed exactly as
+ * fa_fwd computes q[b] against Nk = seqlens_k[b] keys (bottom-right causal alignment, so with
+ * Nq = 1 the query sees every key; windows as in fa_fwd); a sequence with no keys gives out = 0 and
+ * lse = -inf. The keys are split over workgroups and the splits merged through the workspace.
+ *
+ * q, out             device [B, Nq, Hq, D] (strides q_*, o_*); fp16 or bf16, out in the same type.
+ * k_cache, v_cache   device. Dense (block_table NULL): [B, max_seqlen_k, Hkv, D] with strides
+ *                    (k_b, k_n, k_h). Paged: [num_pages, page_size, Hkv, D] with k_b / v_b the page
+ *                    stride; key j of sequence b is slot j % page_size of page
+ *                    block_table[b * max_pages_per_seq + j / page_size].
+ * seqlens_k          device int32 [B]: keys of each sequence, clamped on the device to
+ *                    [0, max_seqlen_k] (and to max_pages_per_seq * page_size when paged).
+ * block_table        device int32 [B, max_pages_per_seq] page ids (clamped to [0, num_pages - 1]
+ *                    on the device), or NULL for a dense cache (then page_size, max_pages_per_seq
+ *                    and num_pages are ignored). The clamps keep every access inside the cache
+ *                    whatever the device arrays hold.
+ * lse                device fp32 [B, Hq, Nq] contiguous, or NULL.
+ * workspace          device scratch of at least fa_fwd_kvcache_workspace_bytes(...) bytes, 16-byte
+ *                    aligned, owned by the caller (may be NULL when that is 0).
+ * Errors: FA_ERR_NULL, FA_ERR_SHAPE (sizes < 1, Hq % Hkv, a paged cache with page_size,
+ * max_pages_per_seq or num_pages < 1, or a launch too large), FA_ERR_HEAD_DIM, FA_ERR_WINDOW,
+ * FA_ERR_SCALE, FA_ERR_STRIDES (negative or not 16-byte multiples, overlapping out rows, a
+ * misaligned pointer), FA_ERR_DTYPE (only FA_F16 and FA_BF16), FA_ERR_WORKSPACE, FA_ERR_LAUNCH.
+ * Asynchronous on `stream`; deterministic (the splits are merged in a fixed order).
+ */
+fa_status fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                         const int32_t* seqlens_k, const int32_t* block_table, int B, int Nq, int Hq, int Hkv,
+                         int D, int max_seqlen_k, int page_size, int max_pages_per_seq, int num_pages,
+                         const fa_strides* strides, float softmax_scale, int causal, int window_left,
+                         int window_right, fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/* Bytes of workspace fa_fwd_kvcache needs for these sizes (0 when the keys are not split, and for
+ * invalid sizes). Pure host function. */
+size_t fa_fwd_kvcache_workspace_bytes(int B, int Nq, int Hq, int Hkv, int D, int max_seqlen_k);
+
 /* Element strides of the backward pass's tensors (headdim stride 1). */
 typedef struct fa_bwd_strides {
   int64_t q_b, q_n, q_h;
