@@ -13,6 +13,11 @@ resident in device memory before the timed region. Prints one JSON line.
 ``--workload varlen_...`` times fa_fwd_varlen on a packed batch of sequences of seeded lengths
 (no padding); its FLOPs are the sum of the sequences' own (causal halved).
 
+``--workload decode_*`` times fa_fwd_kvcache: a few new queries per sequence against a dense or
+paged KV cache of seeded lengths. That path is bound by HBM bandwidth, so its line reports GB/s of
+algorithmic traffic (each sequence's keys and values read once, q read, out and lse written)
+against the 8 TB/s peak, with the TFLOP/s alongside.
+
 ``--pass bwd`` times the backward pass (fa_bwd: dq, dk, dv for a seeded N(0, 1) upstream gradient,
 after one forward pass that provides out and lse) on the same workload; its FLOPs are counted as
 2.5 times the forward's (the five products of the method's backward pass).
@@ -211,7 +216,7 @@ def main():
     import torch
 
     import exact_attention_09_amd as fa
-    from exact_attention_09_amd.inputs import VARLEN_WORKLOADS, WORKLOADS, make_inputs
+    from exact_attention_09_amd.inputs import KVCACHE_WORKLOADS, VARLEN_WORKLOADS, WORKLOADS, make_inputs
 
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
@@ -230,6 +235,11 @@ def main():
                           "launches": args.warmup + args.steps}))
         return
 
+    if args.workload in KVCACHE_WORKLOADS:
+        if args.pass_ == "bwd":
+            print(json.dumps({"error": "the KV-cache path is a forward pass"}))
+            sys.exit(2)
+        return bench_kvcache(args, KVCACHE_WORKLOADS[args.workload], dev)
     if args.workload in VARLEN_WORKLOADS:
         if args.pass_ == "bwd":
             print(json.dumps({"error": "the backward pass takes dense [B, N, H, D] batches"}))
@@ -409,6 +419,98 @@ def bench_varlen(args, w, dev):
     if args.cpu_baseline_seconds > 0:
         rec["cpu_baseline"] = cpu_baseline_varlen(w, lengths, q, k, v, cu_q, descale, args.cpu_baseline_seconds)
     print(json.dumps(rec), flush=True)
+
+
+def kvcache_flops(w, lengths):
+    """Metric FLOPs of one fa_fwd_kvcache call: 4 * Hq * D per admitted (query, key) pair."""
+    pairs = 0
+    for n in lengths:
+        pairs += admitted_pairs(w.Nq, n, w.causal, (-1, -1)) if n > 0 else 0
+    return 4.0 * w.Hq * w.D * pairs
+
+
+def bench_kvcache(args, w, dev):
+    """fa_fwd_kvcache on the cache workload w."""
+    import torch
+
+    import exact_attention_09_amd as fa
+    from exact_attention_09_amd.inputs import make_kvcache_inputs
+
+    lengths = w.lengths(0)
+    q, k, v, seqlens, table = make_kvcache_inputs(w.B, w.Nq, w.Hq, w.Hkv, w.D, w.dtype, lengths, w.page_size, seed=0)
+    qd, kd, vd, sd = q.to(dev), k.to(dev), v.to(dev), seqlens.to(dev)
+    td = table.to(dev) if table is not None else None
+    out = torch.empty_like(qd)
+    lse = torch.empty(w.B, w.Hq, w.Nq, dtype=torch.float32, device=dev)
+    max_k = max(lengths)
+    ws = fa.kvcache_workspace(qd, w.Hkv, max_k)
+    scale = w.softmax_scale()
+
+    def step():
+        st = fa.fwd_kvcache_raw(qd, kd, vd, out, lse, sd, td, max_k, causal=w.causal, softmax_scale=scale,
+                                workspace=ws)
+        if st != 0:
+            raise fa.FaError(st, fa.status_str(st))
+
+    ms_per_step, avg_s, med_s = timed(step, args, torch.cuda.current_stream(dev))
+    flops = kvcache_flops(w, lengths)
+    es = 2
+    kv_bytes = 2 * sum(lengths) * w.Hkv * w.D * es
+    alg_bytes = kv_bytes + 2 * w.B * w.Nq * w.Hq * w.D * es + w.B * w.Hq * w.Nq * 4
+    value = alg_bytes / (ms_per_step / 1e3) / 1e9
+    achieved = alg_bytes / avg_s / 1e9
+    rec = {
+        "metric": "decode attention against a KV cache: algorithmic HBM GB/s (K/V read once)", "value": round(value, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "sequences": w.B, "Nq": w.Nq, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+                   "page_size": w.page_size, "causal": w.causal, "total_keys": sum(lengths),
+                   "min_len": min(lengths), "max_len": max_k, "softmax_scale": scale, "metric_flops": flops},
+        "tflops": round(flops / (ms_per_step / 1e3) / 1e12, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": committed_traffic(w.name, "decode"),
+                     "kernel_avg_us": round(avg_s * 1e6, 3), "kernel_median_us": round(med_s * 1e6, 3),
+                     "algorithmic_bytes": alg_bytes},
+    }
+    if args.cpu_baseline_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline_kvcache(w, lengths, q, k, v, table, args.cpu_baseline_seconds, alg_bytes)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline_kvcache(w, lengths, q, k, v, table, budget_s, alg_bytes):
+    """The KV-cache oracle on whole sequences until budget_s has passed, in the same GB/s metric."""
+    import numpy as np
+    import torch
+
+    from oracle import attention_kvcache_fp64, decode_bf16_bits, decode_f16_bits
+
+    def dec(x):
+        x = x.contiguous()
+        if x.dtype == torch.float16:
+            return decode_f16_bits(x.view(torch.int16).numpy().view(np.uint16))
+        return decode_bf16_bits(x.view(torch.int16).numpy().view(np.uint16))
+
+    done_bytes, n_seq = 0.0, 0
+    t0 = time.perf_counter()
+    elapsed = 0.0
+    for b, n in enumerate(lengths):
+        if table is not None:
+            npg = (n + w.page_size - 1) // w.page_size
+            pages = table[b, :npg].long()
+            kb, vb, tb = dec(k[pages]), dec(v[pages]), np.arange(npg)[None]
+        else:
+            kb, vb, tb = dec(k[b:b + 1, :n]), dec(v[b:b + 1, :n]), None
+        attention_kvcache_fp64(dec(q[b:b + 1]), kb, vb, [n], tb, w.page_size, w.softmax_scale(), w.causal)
+        done_bytes += alg_bytes * n / sum(lengths)
+        n_seq += 1
+        elapsed = time.perf_counter() - t0
+        if elapsed >= budget_s:
+            break
+    threads, blas_name = blas_threads()
+    return {"value": done_bytes / elapsed / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_seq} of {len(lengths)} sequences of the same inputs (all heads), fp64, {elapsed:.1f} s wall; "
+                      f"their share of the algorithmic bytes / wall time; BLAS={blas_name} threads={threads}, "
+                      f"host logical CPUs={os.cpu_count()}"}
 
 
 def cpu_baseline_varlen(w, lengths, q, k, v, cu_q, descale, budget_s):

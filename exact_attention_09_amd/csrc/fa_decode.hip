@@ -35,7 +35,7 @@ __device__ inline int dec_len(const DecArgs& a, int b) {
   return n < 0 ? 0 : (n > cap ? cap : n);
 }
 
-template <class TR, int D>
+template <class TR, int D, bool PAGED>
 __global__ void __launch_bounds__(64) fa_decode_kernel(DecArgs a) {
   using T = OpTile<D>;
   constexpr int ES = 2, KS = D / 16, DB = D / 32;
@@ -76,29 +76,34 @@ __global__ void __launch_bounds__(64) fa_decode_kernel(DecArgs a) {
       qop[ks] = *(const i32x4*)((const char*)a.q + (b * a.q_b + qi * a.q_n + h * a.q_h + ks * 16 + hl * 8) * ES);
   }
 
-  // K or V row of key j (a lane's own key): 64-bit address of its first element
-  auto row_addr = [&](const void* cache, int64_t sb, int64_t sn, int64_t sh, int j) {
-    int64_t row;
-    if (a.block_table != nullptr) {
-      int pg = a.block_table[(int64_t)b * a.max_pages + j / a.page_size];
+  // Blocks of 32 keys jb, jb + 32, ... below je. Lane l32 loads key j0 + l32 of a block (clamped
+  // to the split's last key: keys past it are masked, and their V rows are real, finite cache rows,
+  // so p = 0 meets a finite V). A block's K and V go to one of three register buffers two blocks
+  // ahead of its use; with a paged cache the lane's page id is read one block before that.
+  // Loads run unconditionally (blocks past the last one reload it): with no branch around them the
+  // compiler's wait counts stay exact, and a page id is clamped only where it is used.
+  const int nblk = jb < je ? (je - jb + 31) / 32 : 0;
+  const int* table_row = PAGED ? a.block_table + (int64_t)b * a.max_pages : nullptr;
+  auto key_of = [&](int m) { return min(jb + min(m, nblk - 1) * 32 + l32, k_end - 1); };
+  auto load_page = [&](int m) { return PAGED ? table_row[key_of(m) / a.page_size] : 0; };
+  auto load_block = [&](int m, int pg, i32x4 (&kr)[KS], i32x4 (&vr)[KS]) {
+    const int j = key_of(m);
+    int64_t krow, vrow;
+    if (PAGED) {
       pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
-      row = pg * sb + (int64_t)(j % a.page_size) * sn;
+      const int slot = j % a.page_size;
+      krow = pg * a.k_b + (int64_t)slot * a.k_n;
+      vrow = pg * a.v_b + (int64_t)slot * a.v_n;
     } else {
-      row = b * sb + (int64_t)j * sn;
+      krow = b * a.k_b + (int64_t)j * a.k_n;
+      vrow = b * a.v_b + (int64_t)j * a.v_n;
     }
-    return (const char*)cache + (row + hk * sh) * ES;
-  };
-  // one 32-key block: lane l32's key, head-dim chunks ks*16 + hl*8 (keys past the split read 0,
-  // so that their P = 0 meets V = 0)
-  auto load_block = [&](int j0, i32x4 (&kr)[KS], i32x4 (&vr)[KS]) {
-    const int j = j0 + l32;
-    const bool ok = j < k_end;
-    const char* ka = row_addr(a.kc, a.k_b, a.k_n, a.k_h, ok ? j : 0);
-    const char* va = row_addr(a.vc, a.v_b, a.v_n, a.v_h, ok ? j : 0);
+    const char* ka = (const char*)a.kc + (krow + hk * a.k_h + hl * 8) * ES;
+    const char* va = (const char*)a.vc + (vrow + hk * a.v_h + hl * 8) * ES;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      kr[ks] = ok ? *(const i32x4*)(ka + (ks * 16 + hl * 8) * ES) : i32x4{};
-      vr[ks] = ok ? *(const i32x4*)(va + (ks * 16 + hl * 8) * ES) : i32x4{};
+      kr[ks] = *(const i32x4*)(ka + ks * 16 * ES);
+      vr[ks] = *(const i32x4*)(va + ks * 16 * ES);
     }
   };
 
@@ -117,22 +122,24 @@ __global__ void __launch_bounds__(64) fa_decode_kernel(DecArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
 
-  i32x4 kc[KS], vc[KS];
-  if (jb < je) load_block(jb, kc, vc);
-  for (int j0 = jb; j0 < je; j0 += 32) {
-    // V(j0) into the wave's tile (row l32, chunk 2 ks + hl); the wave's own later transpose reads
+  // block n: read the page of block n + 3 (into `pg_next`), issue the loads of block n + 2 (into
+  // `nk`, `nv`, with page `pg_issue`), then compute block n from `ck`, `cv`. The page read goes
+  // first: loads complete in issue order as far as the wait counter is concerned, so waiting for
+  // it in the next step leaves block n + 2's loads in flight.
+  auto step = [&](int n, const i32x4 (&ck)[KS], const i32x4 (&cv)[KS], i32x4 (&nk)[KS], i32x4 (&nv)[KS],
+                  int pg_issue, int& pg_next) {
+    pg_next = load_page(n + 3);
+    load_block(n + 2, pg_issue, nk, nv);
+    const int j0 = jb + n * 32;
+    // V(j0) into the wave's tile (row l32, chunk 2 ks + hl); the wave's own transpose reads below
     // are ordered after these writes by the LDS queue
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      *(__attribute__((address_space(3))) i32x4*)(uintptr_t)(vt + T::row_off(l32, ks, hl)) = vc[ks];
-    i32x4 kn[KS], vn[KS];
-    const bool more = j0 + 32 < je;
-    if (more) load_block(j0 + 32, kn, vn);
-
+      *(__attribute__((address_space(3))) i32x4*)(uintptr_t)(vt + T::row_off(l32, ks, hl)) = cv[ks];
     f32x16 sc = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) sc = TR::mfma(kc[ks], qop[ks], sc);
-    // accumulator r: key j0 + (r/4)*8 + hl*4 + r%4 for this lane's row
+    for (int ks = 0; ks < KS; ++ks) sc = TR::mfma(ck[ks], qop[ks], sc);
+    // accumulator e: key j0 + (e/4)*8 + hl*4 + e%4 for this lane's row
     const bool full = j0 >= all_lo && j0 + 31 <= all_hi && j0 + 31 < k_end;
     if (!full) {
 #pragma unroll
@@ -168,13 +175,24 @@ __global__ void __launch_bounds__(64) fa_decode_kernel(DecArgs a) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] = TR::mfma(tr_operand<D>(vbase, 0, half, db), pop, o[db]);
     }
-    if (more) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        kc[ks] = kn[ks];
-        vc[ks] = vn[ks];
-      }
-    }
+  };
+
+  i32x4 k0[KS], v0[KS], k1[KS], v1[KS], k2[KS], v2[KS];
+  int pg0 = 0, pg1 = 0, pg2 = 0;
+  if (nblk > 0) {
+    pg0 = load_page(0);
+    pg1 = load_page(1);
+    pg2 = load_page(2);
+    load_block(0, pg0, k0, v0);
+    load_block(1, pg1, k1, v1);
+  }
+  // three blocks per trip, each buffer in a fixed role: no register copies between blocks
+  for (int n = 0; n < nblk; n += 3) {
+    step(n, k0, v0, k2, v2, pg2, pg0);
+    if (n + 1 >= nblk) break;
+    step(n + 1, k1, v1, k0, v0, pg0, pg1);
+    if (n + 2 >= nblk) break;
+    step(n + 2, k2, v2, k1, v1, pg1, pg2);
   }
 
   if (!row_ok) return;
@@ -251,7 +269,10 @@ __global__ void __launch_bounds__(256) fa_decode_merge_kernel(DecArgs a) {
 template <class TR, int D>
 static hipError_t launch_decode_t(const DecArgs& a, hipStream_t stream) {
   const int64_t units = (int64_t)a.B * a.Hkv * a.row_blocks * a.n_split;
-  hipLaunchKernelGGL((fa_decode_kernel<TR, D>), dim3((unsigned)units), dim3(64), 0, stream, a);
+  if (a.block_table != nullptr)
+    hipLaunchKernelGGL((fa_decode_kernel<TR, D, true>), dim3((unsigned)units), dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fa_decode_kernel<TR, D, false>), dim3((unsigned)units), dim3(64), 0, stream, a);
   if (a.n_split > 1) {
     const int64_t threads = (int64_t)a.B * a.Hq * a.Nq * (D / 8);
     hipLaunchKernelGGL((fa_decode_merge_kernel<TR, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);
