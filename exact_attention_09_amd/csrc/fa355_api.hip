@@ -98,14 +98,17 @@ int64_t bwd_workspace_floats(int B, int Nq, int Nk, int Hq, int Hkv, int D) {
 namespace {
 
 // Key splits of fa_fwd_kvcache: enough waves to cover the chip several times over (one wave per
-// (batch, K/V head, row block, split)), splits of at least kDecMinKeys keys, a multiple of 32.
+// (batch, K/V head, row block, split)), splits of kDecMinKeys to kDecMaxKeys keys, a multiple of 32
+// (the upper bound keeps a split's page ids within a few KB of LDS).
 constexpr int64_t kDecTargetWaves = 4096;
 constexpr int kDecMinKeys = 256;
+constexpr int kDecMaxKeys = 4096;
 void dec_split(int B, int Hkv, int row_blocks, int max_seqlen_k, int* n_split, int* split_keys) {
   const int64_t base = (int64_t)B * Hkv * row_blocks;
   const int64_t want = (kDecTargetWaves + base - 1) / base;
   int64_t keys = ((int64_t)max_seqlen_k + want - 1) / want;
   keys = keys < kDecMinKeys ? kDecMinKeys : (keys + 31) / 32 * 32;
+  keys = keys > kDecMaxKeys ? kDecMaxKeys : keys;
   *split_keys = (int)keys;
   *n_split = (int)(((int64_t)max_seqlen_k + keys - 1) / keys);
 }
@@ -370,6 +373,7 @@ fa_status fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache
   a.wr = window_right;
   a.row_blocks = (a.group * Nq + 31) / 32;
   dec_split(B, Hkv, a.row_blocks, max_seqlen_k, &a.n_split, &a.split_keys);
+  a.pages_per_split = block_table ? a.split_keys / page_size + 2 : 0;
   a.q_b = s->q_b; a.q_n = s->q_n; a.q_h = s->q_h;
   a.k_b = s->k_b; a.k_n = s->k_n; a.k_h = s->k_h;
   a.v_b = s->v_b; a.v_n = s->v_n; a.v_h = s->v_h;

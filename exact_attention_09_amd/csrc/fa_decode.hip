@@ -40,7 +40,15 @@ __global__ void __launch_bounds__(64) fa_decode_kernel(DecArgs a) {
   using T = OpTile<D>;
   constexpr int ES = 2, KS = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(16))) char vtile[32 * T::ROWB];   // the wave's 32 V rows
+  // the wave's 32 query rows can be read back from LDS for every block instead of kept in
+  // registers (measured no faster: off)
+  constexpr bool Q_IN_LDS = false;
+  __shared__ __attribute__((aligned(16))) char qtile[Q_IN_LDS ? 32 * T::ROWB : 16];
+  extern __shared__ int ptab[];   // paged cache: the page ids of this split (pages_per_split)
 
+  // register buffers: blocks in flight two ahead of their use (at D = 128 this takes the kernel
+  // past 256 registers, to one wave per SIMD; one buffer fewer measured slower all the same)
+  constexpr int NB = 3;
   const int lane = threadIdx.x, hl = lane >> 5, l32 = lane & 31;
   int u = blockIdx.x;
   const int s = u % a.n_split;
@@ -75,22 +83,37 @@ __global__ void __launch_bounds__(64) fa_decode_kernel(DecArgs a) {
     if (row_ok)
       qop[ks] = *(const i32x4*)((const char*)a.q + (b * a.q_b + qi * a.q_n + h * a.q_h + ks * 16 + hl * 8) * ES);
   }
+  const uint32_t qt = lds_addr_of(qtile);
+  if constexpr (Q_IN_LDS) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      *(__attribute__((address_space(3))) i32x4*)(uintptr_t)(qt + T::row_off(l32, ks, hl)) = qop[ks];
+  }
 
   // Blocks of 32 keys jb, jb + 32, ... below je. Lane l32 loads key j0 + l32 of a block (clamped
   // to the split's last key: keys past it are masked, and their V rows are real, finite cache rows,
-  // so p = 0 meets a finite V). A block's K and V go to one of three register buffers two blocks
-  // ahead of its use; with a paged cache the lane's page id is read one block before that.
-  // Loads run unconditionally (blocks past the last one reload it): with no branch around them the
-  // compiler's wait counts stay exact, and a page id is clamped only where it is used.
+  // so p = 0 meets a finite V). A block's K and V go to one of NB register buffers, NB - 1 blocks
+  // ahead of its use. Loads run unconditionally (blocks past the last one reload it): with no
+  // branch around them the compiler's wait counts stay exact. With a paged cache the split's page
+  // ids are first copied to LDS (one HBM round trip per split instead of one per block).
   const int nblk = jb < je ? (je - jb + 31) / 32 : 0;
-  const int* table_row = PAGED ? a.block_table + (int64_t)b * a.max_pages : nullptr;
   auto key_of = [&](int m) { return min(jb + min(m, nblk - 1) * 32 + l32, k_end - 1); };
-  auto load_page = [&](int m) { return PAGED ? table_row[key_of(m) / a.page_size] : 0; };
-  auto load_block = [&](int m, int pg, i32x4 (&kr)[KS], i32x4 (&vr)[KS]) {
+  const int first_page = PAGED && nblk > 0 ? k_begin / a.page_size : 0;
+  if constexpr (PAGED) {
+    if (nblk > 0) {
+      const int* table_row = a.block_table + (int64_t)b * a.max_pages;
+      const int ne = (k_end - 1) / a.page_size - first_page + 1;   // <= pages_per_split
+      for (int e = lane; e < ne; e += 64) {
+        const int pg = table_row[first_page + e];
+        ptab[e] = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+      }
+    }
+  }
+  auto load_block = [&](int m, i32x4 (&kr)[KS], i32x4 (&vr)[KS]) {
     const int j = key_of(m);
     int64_t krow, vrow;
-    if (PAGED) {
-      pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+    if constexpr (PAGED) {
+      const int pg = ptab[j / a.page_size - first_page];
       const int slot = j % a.page_size;
       krow = pg * a.k_b + (int64_t)slot * a.k_n;
       vrow = pg * a.v_b + (int64_t)slot * a.v_n;
@@ -122,14 +145,10 @@ __global__ void __launch_bounds__(64) fa_decode_kernel(DecArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = f32x16{};
 
-  // block n: read the page of block n + 3 (into `pg_next`), issue the loads of block n + 2 (into
-  // `nk`, `nv`, with page `pg_issue`), then compute block n from `ck`, `cv`. The page read goes
-  // first: loads complete in issue order as far as the wait counter is concerned, so waiting for
-  // it in the next step leaves block n + 2's loads in flight.
-  auto step = [&](int n, const i32x4 (&ck)[KS], const i32x4 (&cv)[KS], i32x4 (&nk)[KS], i32x4 (&nv)[KS],
-                  int pg_issue, int& pg_next) {
-    pg_next = load_page(n + 3);
-    load_block(n + 2, pg_issue, nk, nv);
+  // block n: issue the loads of block n + NB - 1 (into `nk`, `nv`), then compute block n from
+  // `ck`, `cv`
+  auto step = [&](int n, const i32x4 (&ck)[KS], const i32x4 (&cv)[KS], i32x4 (&nk)[KS], i32x4 (&nv)[KS]) {
+    load_block(n + NB - 1, nk, nv);
     const int j0 = jb + n * 32;
     // V(j0) into the wave's tile (row l32, chunk 2 ks + hl); the wave's own transpose reads below
     // are ordered after these writes by the LDS queue
@@ -138,7 +157,11 @@ __global__ void __launch_bounds__(64) fa_decode_kernel(DecArgs a) {
       *(__attribute__((address_space(3))) i32x4*)(uintptr_t)(vt + T::row_off(l32, ks, hl)) = cv[ks];
     f32x16 sc = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) sc = TR::mfma(ck[ks], qop[ks], sc);
+    for (int ks = 0; ks < KS; ++ks) {
+      i32x4 qk = qop[ks];
+      if constexpr (Q_IN_LDS) qk = lds_read_b128(qt + T::row_off(l32, ks, hl));
+      sc = TR::mfma(ck[ks], qk, sc);
+    }
     // accumulator e: key j0 + (e/4)*8 + hl*4 + e%4 for this lane's row
     const bool full = j0 >= all_lo && j0 + 31 <= all_hi && j0 + 31 < k_end;
     if (!full) {
@@ -177,22 +200,26 @@ __global__ void __launch_bounds__(64) fa_decode_kernel(DecArgs a) {
     }
   };
 
+  // NB register buffers per trip, each in a fixed role: no register copies between blocks
   i32x4 k0[KS], v0[KS], k1[KS], v1[KS], k2[KS], v2[KS];
-  int pg0 = 0, pg1 = 0, pg2 = 0;
   if (nblk > 0) {
-    pg0 = load_page(0);
-    pg1 = load_page(1);
-    pg2 = load_page(2);
-    load_block(0, pg0, k0, v0);
-    load_block(1, pg1, k1, v1);
+    load_block(0, k0, v0);
+    if constexpr (NB == 3) load_block(1, k1, v1);
   }
-  // three blocks per trip, each buffer in a fixed role: no register copies between blocks
-  for (int n = 0; n < nblk; n += 3) {
-    step(n, k0, v0, k2, v2, pg2, pg0);
-    if (n + 1 >= nblk) break;
-    step(n + 1, k1, v1, k0, v0, pg0, pg1);
-    if (n + 2 >= nblk) break;
-    step(n + 2, k2, v2, k1, v1, pg1, pg2);
+  if constexpr (NB == 3) {
+    for (int n = 0; n < nblk; n += 3) {
+      step(n, k0, v0, k2, v2);
+      if (n + 1 >= nblk) break;
+      step(n + 1, k1, v1, k0, v0);
+      if (n + 2 >= nblk) break;
+      step(n + 2, k2, v2, k1, v1);
+    }
+  } else {
+    for (int n = 0; n < nblk; n += 2) {
+      step(n, k0, v0, k1, v1);
+      if (n + 1 >= nblk) break;
+      step(n + 1, k1, v1, k0, v0);
+    }
   }
 
   if (!row_ok) return;
@@ -270,7 +297,8 @@ template <class TR, int D>
 static hipError_t launch_decode_t(const DecArgs& a, hipStream_t stream) {
   const int64_t units = (int64_t)a.B * a.Hkv * a.row_blocks * a.n_split;
   if (a.block_table != nullptr)
-    hipLaunchKernelGGL((fa_decode_kernel<TR, D, true>), dim3((unsigned)units), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL((fa_decode_kernel<TR, D, true>), dim3((unsigned)units), dim3(64),
+                       (size_t)a.pages_per_split * 4, stream, a);
   else
     hipLaunchKernelGGL((fa_decode_kernel<TR, D, false>), dim3((unsigned)units), dim3(64), 0, stream, a);
   if (a.n_split > 1) {

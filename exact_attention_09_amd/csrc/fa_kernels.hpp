@@ -117,6 +117,7 @@ struct DecArgs {
   int causal, wl, wr;
   int row_blocks;            // ceil(group * Nq / 32): the group's query rows, 32 per wave
   int n_split, split_keys;   // splits per (batch, K/V head, row block); keys per split (a multiple of 32)
+  int pages_per_split;       // paged: page ids one split can span (split_keys / page_size + 2)
   int64_t q_b, q_n, q_h, k_b, k_n, k_h, v_b, v_n, v_h, o_b, o_n, o_h;   // k_b, v_b: page stride when paged
   float scale_log2;
 };
