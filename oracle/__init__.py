@@ -24,19 +24,24 @@ Contents:
     sequence of a packed variable-length batch.
   * :mod:`oracle.kvcache` — ``attention_kvcache_fp64``: queries against each sequence's keys in
     a dense or paged key/value cache (the decode-shaped workload).
+  * :mod:`oracle.blocksparse` — ``attention_blocksparse_fp64``: the definition restricted to the
+    (query block, key block) pairs a block mask sets.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against closed forms, invariants,
 the worked example, brute force and an independent library routine.
 """
 from .attention import admitted, attention_fp64, attention_rows_fp64, kv_head_of, tiled_online_fp64
 from .backward import attention_bwd_fp64
+from .blocksparse import attention_blocksparse_fp64, block_admitted
 from .formats import decode_bf16_bits, decode_e4m3_codes, decode_f16_bits, e4m3_table
 from .kvcache import attention_kvcache_fp64, gather_kv
 from .varlen import attention_varlen_fp64
 
 __all__ = [
     "admitted",
+    "attention_blocksparse_fp64",
     "attention_bwd_fp64",
+    "block_admitted",
     "attention_fp64",
     "attention_kvcache_fp64",
     "gather_kv",
