@@ -37,6 +37,7 @@ hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, int64_t grid, hipStrea
 namespace {
 
 constexpr int kMaxSeq = 1 << 30;
+constexpr int kMaxSparseKeyBlocks = 4096;   // block-sparse: key blocks of one row (LDS tile list)
 constexpr int64_t kMaxSpan = (int64_t)1 << 31;
 constexpr int kSpanSlack = 256;  // rows a tile may reach past the end of a sequence
 
@@ -203,9 +204,15 @@ fa_status fa_fwd_plan(int B, int Nq, int Nk, int Hq, int Hkv, int D, int causal,
   return FA_OK;
 }
 
-fa_status fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Nq, int Nk, int Hq,
-                 int Hkv, int D, const fa_strides* s, float softmax_scale, int causal, int window_left,
-                 int window_right, fa_dtype dtype, hipStream_t stream, const float* descale_qkv) {
+}  // extern "C"
+
+namespace {
+
+// fa_fwd, and fa_fwd_blocksparse when block_mask is set.
+fa_status fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Nq, int Nk, int Hq,
+                   int Hkv, int D, const fa_strides* s, float softmax_scale, int causal, int window_left,
+                   int window_right, fa_dtype dtype, hipStream_t stream, const float* descale_qkv,
+                   const uint8_t* block_mask, int mask_heads) {
   if (!q || !k || !v || !out || !s) return FA_ERR_NULL;
   fa_status st = check_sizes(B, Nq, Nk, Hq, Hkv, D, window_left, window_right, dtype);
   if (st != FA_OK) return st;
@@ -257,11 +264,39 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* out, float* 
   a.out_scale = dtype == FA_FP8_E4M3 ? dv : 1.f;
   a.cu_q = a.cu_k = nullptr;
   a.total_q = a.total_k = 0;
+  a.block_mask = block_mask;
+  a.mask_heads = mask_heads;
+  a.nqb = (Nq + fa::kSparseBlockQ - 1) / fa::kSparseBlockQ;
+  a.nkb = (Nk + fa::kSparseBlockK - 1) / fa::kSparseBlockK;
   const fa::TileShape ts = fa::tile_shape(D, dtype);
   a.num_q_tiles = (Nq + ts.block_m - 1) / ts.block_m;
   const int64_t grid = (int64_t)B * Hq * a.num_q_tiles;
   const hipError_t e = fa::launch_fwd(a, D, dtype, grid, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Nq, int Nk, int Hq,
+                 int Hkv, int D, const fa_strides* s, float softmax_scale, int causal, int window_left,
+                 int window_right, fa_dtype dtype, hipStream_t stream, const float* descale_qkv) {
+  return fwd_impl(q, k, v, out, lse, B, Nq, Nk, Hq, Hkv, D, s, softmax_scale, causal, window_left, window_right,
+                  dtype, stream, descale_qkv, nullptr, 0);
+}
+
+fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Nq,
+                             int Nk, int Hq, int Hkv, int D, const fa_strides* s, float softmax_scale, int causal,
+                             int window_left, int window_right, fa_dtype dtype, hipStream_t stream,
+                             const uint8_t* block_mask, int mask_heads) {
+  if (!block_mask) return FA_ERR_NULL;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (mask_heads != 1 && mask_heads != Hq) return FA_ERR_SHAPE;
+  // the tile list of a workgroup lives in LDS next to the K/V rings
+  if ((int64_t)Nk > (int64_t)kMaxSparseKeyBlocks * fa::kSparseBlockK) return FA_ERR_SHAPE;
+  return fwd_impl(q, k, v, out, lse, B, Nq, Nk, Hq, Hkv, D, s, softmax_scale, causal, window_left, window_right,
+                  dtype, stream, nullptr, block_mask, mask_heads);
 }
 
 fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, float* lse, const int32_t* cu_seqlens_q,
@@ -322,6 +357,8 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, 
   a.out_scale = dtype == FA_FP8_E4M3 ? dv : 1.f;
   a.cu_q = cu_seqlens_q;
   a.cu_k = cu_seqlens_k;
+  a.block_mask = nullptr;
+  a.mask_heads = a.nqb = a.nkb = 0;
   a.total_q = total_q;
   a.total_k = total_k;
   const fa::TileShape ts = fa::tile_shape(D, dtype);

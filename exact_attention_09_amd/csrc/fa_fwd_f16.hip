@@ -42,7 +42,7 @@
 
 namespace fa {
 
-template <class TR, int D, int BN, int WAVES>
+template <class TR, int D, int BN, int WAVES, bool SP>
 __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   constexpr int NT = WAVES * 64;        // threads per workgroup
   constexpr int BM = WAVES * 32;        // query rows per workgroup
@@ -113,6 +113,49 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   const int lo_i = clamp_key(key_lo(ms, my_row));
   const int hi_i = clamp_key(key_hi(ms, my_row));
   const uint32_t span_i = hi_i >= lo_i ? (uint32_t)(hi_i - lo_i + 1) : 0u;
+
+  // ---- block-sparse: the tiles of [tb, te) that the block mask sets for one of the workgroup's
+  // mask rows, compacted into LDS by wave 0 (sp_list: tile ids, then a bit per mask row, then the
+  // count). Steps then run over positions 0 .. n of this list instead of tiles tb .. te, and a
+  // tile whose bit is clear for a wave's own mask row is masked entirely for that wave.
+  extern __shared__ int sp_list[];
+  int sp_n = 0, sp_row = 0;
+  if constexpr (SP) {
+    const int mr0 = q0 / kSparseBlockQ;
+    const int nrows = min(BM / kSparseBlockQ, a.nqb - mr0);
+    sp_row = (q0 + wave * 32) / kSparseBlockQ - mr0;
+    const uint8_t* mrow = a.block_mask + ((int64_t)(a.mask_heads == 1 ? 0 : h) * a.nqb + mr0) * a.nkb;
+    if (wave == 0) {
+      int cnt = 0;
+      for (int base = tb; base < te; base += 64) {
+        const int t = base + lane;
+        int bits = 0;
+        if (t < te)
+          for (int r = 0; r < nrows; ++r) bits |= (mrow[(int64_t)r * a.nkb + t] != 0) << r;
+        const uint64_t set = __builtin_amdgcn_ballot_w64(bits != 0);
+        const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(set >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)set, 0));
+        if (bits != 0) {
+          sp_list[pos] = t;
+          sp_list[a.nkb + pos] = bits;
+        }
+        cnt += __builtin_popcountll(set);
+      }
+      if (lane == 0) sp_list[2 * a.nkb] = cnt;
+    }
+    __syncthreads();
+    sp_n = __builtin_amdgcn_readfirstlane(sp_list[2 * a.nkb]);
+  }
+  // tile of step position p (SP) and whether this wave's mask row admits it; positions past the
+  // list map to a tile past every key, which the element masks clear entirely
+  auto sp_tile = [&](int p) {
+    const int t = __builtin_amdgcn_readfirstlane(sp_list[p < sp_n ? p : 0]);   // index kept in range
+    return p < sp_n ? t : te + 2;
+  };
+  auto sp_admits = [&](int p) {
+    const int bits = __builtin_amdgcn_readfirstlane(sp_list[a.nkb + (p < sp_n ? p : 0)]);
+    return p < sp_n && ((bits >> sp_row) & 1);
+  };
+  const int pb0 = SP ? 0 : tb, pe = SP ? sp_n : te;   // step positions pb0 .. pe
 
   // Q operands (B operand of S^T): row my_row, head-dim slots ks*16 + hl*8 .. +7; loaded in the
   // prologue, behind the first K/V tile loads
@@ -254,11 +297,13 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int c = tid * 16; c < TILEB; c += NT * 16) *(i32x4*)(vring + 2 * TILEB + c) = i32x4{};
   // prologue: K(tb), K(tb+1), V(tb), K(tb+2) in flight; K(tb) and K(tb+1) landed; S(tb)
-  if (tb < te) {
-    dma(k_d, kgoff, (uint32_t)(tb * BN) * k_rowb, kring_a);
-    if (tb + 1 < te) dma(k_d, kgoff, (uint32_t)((tb + 1) * BN) * k_rowb, kring_a + TILEB);
-    dma(v_d, vgoff, (uint32_t)(tb * BN) * v_rowb, vring_a);
-    if (tb + 2 < te) dma(k_d, kgoff, (uint32_t)((tb + 2) * BN) * k_rowb, kring_a + 2 * TILEB);
+  // (positions 0, 1, 2 of the tile list when block-sparse)
+  if (pb0 < pe) {
+    const int t0 = SP ? sp_tile(0) : tb, t1 = SP ? sp_tile(1) : tb + 1, t2 = SP ? sp_tile(2) : tb + 2;
+    dma(k_d, kgoff, (uint32_t)(t0 * BN) * k_rowb, kring_a);
+    if (pb0 + 1 < pe) dma(k_d, kgoff, (uint32_t)(t1 * BN) * k_rowb, kring_a + TILEB);
+    dma(v_d, vgoff, (uint32_t)(t0 * BN) * v_rowb, vring_a);
+    if (pb0 + 2 < pe) dma(k_d, kgoff, (uint32_t)(t2 * BN) * k_rowb, kring_a + 2 * TILEB);
   }
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks)
@@ -287,11 +332,21 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   barrier_keep(0);   // every wave has read K(tb) before step tb refills its slot
 
   auto step = [&](int j, f32x16 (&sc)[KB], f32x16 (&sn)[KB], const uint32_t (&pp)[KB][8], uint32_t (&pc)[KB][8]) {
-    const bool k3 = j + 3 < te, v1 = j + 1 < te;
-    if (k3) dma(k_d, kgoff, k_soff, kring_a + r0);
-    if (v1) dma(v_d, vgoff, v_soff, vring_a + r1);
-    if ((uint32_t)(j - need_lo) < need_n) {
-      if (!((uint32_t)(j - flo) < full_n)) mask_tile(sc, j);
+    const bool k3 = j + 3 < pe, v1 = j + 1 < pe;
+    if (k3) dma(k_d, kgoff, SP ? (uint32_t)(sp_tile(j + 3) * BN) * k_rowb : k_soff, kring_a + r0);
+    if (v1) dma(v_d, vgoff, SP ? (uint32_t)(sp_tile(j + 1) * BN) * v_rowb : v_soff, vring_a + r1);
+    if (SP || (uint32_t)(j - need_lo) < need_n) {
+      if constexpr (SP) {
+        const int tj = sp_tile(j);
+        if (!sp_admits(j)) {
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) sc[kb] = f32x16{} - INFINITY;
+        } else if (!((uint32_t)(tj - flo) < full_n)) {
+          mask_tile(sc, tj);
+        }
+      } else {
+        if (!((uint32_t)(j - flo) < full_n)) mask_tile(sc, j);
+      }
       // Operand of MFMA e of the sequence (even e: S, K from LDS; odd e: PV, V^T from LDS), read
       // PF MFMAs ahead of its use. At D = 64 every read is issued up front (registers allow it
       // and it measured fastest); at D = 128 a short distance keeps the kernel within 256
@@ -354,11 +409,11 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
 
   // Steps tb .. te; the last one only drains PV(te-1). Two steps per trip swap the roles of the
   // S and P arrays; the exits after either step keep the loop-carried values in place.
-  for (int t = tb;; t += 2) {
+  for (int t = pb0;; t += 2) {
     step(t, sa, sb, pb, pa);
-    if (t + 1 > te) break;
+    if (t + 1 > pe) break;
     step(t + 1, sb, sa, pa, pb);
-    if (t + 2 > te) break;
+    if (t + 2 > pe) break;
   }
 
   // ---- epilogue: O / l, lse = (m + log2 l) * ln 2
@@ -383,7 +438,12 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
 template <class TR, int D>
 static hipError_t launch_t(const FwdArgs& a, int64_t grid, hipStream_t stream) {
   constexpr int BN = 64, WAVES = D == 64 ? 4 : 8;
-  hipLaunchKernelGGL((fa_fwd_kernel<TR, D, BN, WAVES>), dim3((unsigned)grid), dim3(WAVES * 64), 0, stream, a);
+  static_assert(BN == kSparseBlockK && (WAVES * 32) % kSparseBlockQ == 0, "tiles nest in the mask's blocks");
+  if (a.block_mask != nullptr)
+    hipLaunchKernelGGL((fa_fwd_kernel<TR, D, BN, WAVES, true>), dim3((unsigned)grid), dim3(WAVES * 64),
+                       (size_t)(2 * a.nkb + 1) * 4, stream, a);
+  else
+    hipLaunchKernelGGL((fa_fwd_kernel<TR, D, BN, WAVES, false>), dim3((unsigned)grid), dim3(WAVES * 64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -30,7 +30,14 @@ struct FwdArgs {
   const int* cu_q;
   const int* cu_k;
   int total_q, total_k;
+  // Block-sparse (null for dense): block_mask[hm, qb, kb] != 0 admits the pairs of query block qb
+  // (kSparseBlockQ rows) and key block kb (kSparseBlockK keys); hm = 0 when mask_heads == 1, else
+  // the query head.
+  const uint8_t* block_mask;
+  int mask_heads, nqb, nkb;
 };
+constexpr int kSparseBlockQ = 128;
+constexpr int kSparseBlockK = 64;
 
 // One workgroup's sequence: its sizes, the element offsets of its row 0 in q, k, v and out (head
 // offsets not included), the lse index of its row 0 for query head h, and its heads' byte spans.

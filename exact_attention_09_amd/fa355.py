@@ -20,7 +20,7 @@ _DTYPE_CODE = {torch.float16: FA_F16, torch.bfloat16: FA_BF16, torch.float8_e4m3
 _OUT_DTYPE = {FA_F16: torch.float16, FA_BF16: torch.bfloat16, FA_FP8_E4M3: torch.bfloat16}
 
 # Every symbol include/fa355.h declares.
-EXPORTED = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str", "fa_fwd_plan", "fa_kv_tile_range", "fa_version")
+EXPORTED = ("fa_fwd", "fa_fwd_blocksparse", "fa_fwd_varlen", "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str", "fa_fwd_plan", "fa_kv_tile_range", "fa_version")
 
 
 class FaStrides(ctypes.Structure):
@@ -64,6 +64,10 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                            c_int, c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(FaStrides),
                            c_float, c_int, c_int, c_int, c_int, c_void_p, ctypes.POINTER(c_float)]
+    lib.fa_fwd_blocksparse.restype = c_int
+    lib.fa_fwd_blocksparse.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                       c_int, c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(FaStrides),
+                                       c_float, c_int, c_int, c_int, c_int, c_void_p, c_void_p, c_int]
     lib.fa_fwd_varlen.restype = c_int
     lib.fa_fwd_varlen.argtypes = [c_void_p] * 7 + [c_int] * 7 + [ctypes.POINTER(FaVarlenStrides), c_float, c_int, c_int,
                                                                   c_int, c_int, c_void_p, ctypes.POINTER(c_float)]
@@ -147,6 +151,45 @@ def fwd(q, k, v, causal=False, window=(-1, -1), softmax_scale=None, descale=None
     if lse is None and return_lse:
         lse = torch.empty(B, Hq, Nq, dtype=torch.float32, device=q.device)
     status = fwd_raw(q, k, v, out, lse, causal, window, softmax_scale, descale)
+    if status != 0:
+        raise FaError(status, status_str(status))
+    return out, lse
+
+
+def fwd_blocksparse_raw(q, k, v, out, lse, block_mask, causal=False, window=(-1, -1), softmax_scale=None,
+                        stream=None) -> int:
+    """Call fa_fwd_blocksparse on caller-provided tensors; returns the status code without raising.
+    ``block_mask``: device uint8 [1 or Hq, ceil(Nq / 128), ceil(Nk / 64)]."""
+    lib = load()
+    code = _DTYPE_CODE.get(q.dtype)
+    if code is None:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    B, Nq, Hq, D = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if block_mask.dtype != torch.uint8 or block_mask.dim() != 3 or not block_mask.is_contiguous():
+        raise ValueError("block_mask must be a contiguous uint8 [mask_heads, nqb, nkb] tensor")
+    nqb, nkb = -(-Nq // 128), -(-Nk // 64)
+    if tuple(block_mask.shape[1:]) != (nqb, nkb):
+        raise ValueError(f"block_mask must be [1 or {Hq}, {nqb}, {nkb}], got {tuple(block_mask.shape)}")
+    scale = float(D) ** -0.5 if softmax_scale is None else float(softmax_scale)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = _strides(q, k, v, out)
+    return lib.fa_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  lse.data_ptr() if lse is not None else None, B, Nq, Nk, Hq, Hkv, D,
+                                  ctypes.byref(st), scale, int(bool(causal)), int(window[0]), int(window[1]), code,
+                                  stream, block_mask.data_ptr(), block_mask.shape[0])
+
+
+def fwd_blocksparse(q, k, v, block_mask, causal=False, window=(-1, -1), softmax_scale=None):
+    """Block-sparse FlashAttention forward: fwd restricted to the (128-row, 64-key) blocks that
+    ``block_mask`` (device uint8 [1 or Hq, ceil(Nq/128), ceil(Nk/64)]) sets. Returns (out, lse)."""
+    if not all(t.is_cuda for t in (q, k, v, block_mask)):
+        raise ValueError("all tensors must be device tensors")
+    B, Nq, Hq, D = q.shape
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Hq, Nq, dtype=torch.float32, device=q.device)
+    status = fwd_blocksparse_raw(q, k, v, out, lse, block_mask, causal, window, softmax_scale)
     if status != 0:
         raise FaError(status, status_str(status))
     return out, lse

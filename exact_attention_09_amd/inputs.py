@@ -225,3 +225,64 @@ KVCACHE_WORKLOADS = {
                         "bf16", causal=True),
     ]
 }
+
+
+# ---- block-sparse attention
+def sparse_block_mask(Nq: int, Nk: int, heads: int, band: int, sinks: int, p_random: float, seed: int,
+                      causal: bool = True):
+    """uint8 [heads, ceil(Nq / 128), ceil(Nk / 64)] block mask of a local + sink + random pattern:
+    for query block r (rows 128 r .. 128 r + 127) the key blocks of the band reaching `band` blocks
+    of 64 keys before its diagonal blocks (2 r, 2 r + 1; keys and queries aligned at the end), the
+    first `sinks` key blocks, and each other key block with probability `p_random` (seeded). With
+    `causal`, blocks entirely after the diagonal are left out."""
+    nqb, nkb = -(-Nq // 128), -(-Nk // 64)
+    off = Nk - Nq
+    g = torch.Generator().manual_seed(30_000 + seed)
+    m = (torch.rand(heads, nqb, nkb, generator=g) < p_random)
+    r = torch.arange(nqb)[:, None]
+    kb = torch.arange(nkb)[None, :]
+    diag_lo = (128 * r + off) // 64            # key block of the block's first row's diagonal
+    diag_hi = (128 * r + 127 + off) // 64
+    m |= ((kb >= diag_lo - band) & (kb <= diag_hi))[None]
+    m |= (kb < sinks)[None]
+    if causal:
+        m &= (kb <= diag_hi)[None]
+    return m.to(torch.uint8)
+
+
+@dataclass(frozen=True)
+class SparseWorkload:
+    name: str
+    B: int
+    N: int
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: str
+    band: int
+    sinks: int
+    p_random: float
+    mask_heads: int = 1
+    causal: bool = True
+    scale: float | None = None
+
+    def softmax_scale(self) -> float:
+        return self.scale if self.scale is not None else self.D ** -0.5
+
+    def mask(self, seed: int = 0):
+        return sparse_block_mask(self.N, self.N, self.mask_heads, self.band, self.sinks, self.p_random, seed,
+                                 self.causal)
+
+
+# The pages' block-sparse claim is for long sequences (64k tokens): a 65 536-token causal
+# sequence with a local band of 512 keys, 2 sink blocks and 5 % random blocks, shared by all 16
+# heads (D = 64, fp16); and a per-head pattern at 16k tokens, D = 128, bf16.
+SPARSE_WORKLOADS = {
+    w.name: w
+    for w in [
+        SparseWorkload("blocksparse_b1_h16_n65536_d64_f16", 1, 65536, 16, 16, 64, "f16", band=8, sinks=2,
+                       p_random=0.05, scale=0.125),
+        SparseWorkload("blocksparse_b1_h32_n16384_d128_bf16_perhead", 1, 16384, 32, 8, 128, "bf16", band=4, sinks=1,
+                       p_random=0.1, mask_heads=32),
+    ]
+}

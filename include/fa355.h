@@ -97,6 +97,27 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* out, float* 
                  float softmax_scale, int causal, int window_left, int window_right,
                  fa_dtype dtype, hipStream_t stream, const float* descale_qkv);
 
+/*
+ * fa_fwd_blocksparse — fa_fwd restricted to the (query block, key block) pairs a block mask sets,
+ * skipping the key tiles no row of a workgroup needs. The pages report a block-sparse variant of
+ * FlashAttention that scales to 64k tokens and runs 2-4 times faster than the dense one ("What
+ * FlashAttention is and how it speeds up attention", FAQ on the quadratic complexity) without an
+ * interface or a pattern; this is the library's reading. Query i and key j are admitted when
+ * block_mask[hm * nqb * nkb + (i / 128) * nkb + j / 64] != 0 and fa_fwd's causal / window rules
+ * admit them; nqb = ceil(Nq / 128), nkb = ceil(Nk / 64); hm = 0 when mask_heads == 1, else the
+ * query head. A row with no admitted key gets out = 0 and lse = -inf.
+ *
+ * block_mask         device uint8 [mask_heads, nqb, nkb], read by the kernel (no host copy).
+ * mask_heads         1 (one mask for every head) or Hq.
+ * dtype              FA_F16 or FA_BF16 (else FA_ERR_DTYPE). Nk <= 4096 * 64 (else FA_ERR_SHAPE).
+ * Other arguments, validation, errors and asynchrony as for fa_fwd.
+ */
+fa_status fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* out, float* lse,
+                             int B, int Nq, int Nk, int Hq, int Hkv, int D, const fa_strides* strides,
+                             float softmax_scale, int causal, int window_left, int window_right,
+                             fa_dtype dtype, hipStream_t stream, const uint8_t* block_mask,
+                             int mask_heads);
+
 /* Element strides of packed variable-length tensors: token and head axes (headdim stride 1). */
 typedef struct fa_varlen_strides {
   int64_t q_n, q_h;
