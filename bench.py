@@ -18,6 +18,10 @@ paged KV cache of seeded lengths. That path is bound by HBM bandwidth, so its li
 algorithmic traffic (each sequence's keys and values read once, q read, out and lse written)
 against the 8 TB/s peak, with the TFLOP/s alongside.
 
+``--workload blocksparse_*`` times fa_fwd_blocksparse on a long causal sequence with a local +
+sink + random block mask; its FLOPs are 4 * D per admitted (query, key) pair, and the dense
+causal forward on the same inputs is timed beside it (speedup).
+
 ``--pass bwd`` times the backward pass (fa_bwd: dq, dk, dv for a seeded N(0, 1) upstream gradient,
 after one forward pass that provides out and lse) on the same workload; its FLOPs are counted as
 2.5 times the forward's (the five products of the method's backward pass).
@@ -216,7 +220,8 @@ def main():
     import torch
 
     import exact_attention_09_amd as fa
-    from exact_attention_09_amd.inputs import KVCACHE_WORKLOADS, VARLEN_WORKLOADS, WORKLOADS, make_inputs
+    from exact_attention_09_amd.inputs import (KVCACHE_WORKLOADS, SPARSE_WORKLOADS, VARLEN_WORKLOADS, WORKLOADS,
+                                               make_inputs)
 
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
@@ -235,6 +240,11 @@ def main():
                           "launches": args.warmup + args.steps}))
         return
 
+    if args.workload in SPARSE_WORKLOADS:
+        if args.pass_ == "bwd":
+            print(json.dumps({"error": "the block-sparse path is a forward pass"}))
+            sys.exit(2)
+        return bench_sparse(args, SPARSE_WORKLOADS[args.workload], dev)
     if args.workload in KVCACHE_WORKLOADS:
         if args.pass_ == "bwd":
             print(json.dumps({"error": "the KV-cache path is a forward pass"}))
@@ -419,6 +429,118 @@ def bench_varlen(args, w, dev):
     if args.cpu_baseline_seconds > 0:
         rec["cpu_baseline"] = cpu_baseline_varlen(w, lengths, q, k, v, cu_q, descale, args.cpu_baseline_seconds)
     print(json.dumps(rec), flush=True)
+
+
+def sparse_pairs(w, mask_heads_mask):
+    """Admitted (query, key) pairs per head of a block mask [hm, nqb, nkb] under w's causal mask."""
+    import numpy as np
+    m = mask_heads_mask.numpy() != 0
+    N = w.N
+    per_head = []
+    r = np.arange(N)
+    for hm in range(m.shape[0]):
+        total = 0
+        for qb in range(m.shape[1]):
+            rows = r[qb * 128:(qb + 1) * 128]
+            for kb in np.nonzero(m[hm, qb])[0]:
+                j0, j1 = kb * 64, min(N, kb * 64 + 64)
+                hi = np.minimum(rows, j1 - 1) if w.causal else np.full(len(rows), j1 - 1)
+                total += int(np.maximum(0, hi - j0 + 1).sum())
+        per_head.append(total)
+    return per_head
+
+
+def bench_sparse(args, w, dev):
+    """fa_fwd_blocksparse on the sparse workload w, with the dense causal forward timed beside it."""
+    import torch
+
+    import exact_attention_09_amd as fa
+    from exact_attention_09_amd.inputs import draw_qkv, to_storage
+
+    q, k, v = draw_qkv(w.B, w.N, w.N, w.Hq, w.Hkv, w.D, seed=0)
+    q, k, v, _ = to_storage(q, k, v, w.dtype)
+    mask = w.mask(0)
+    qd, kd, vd, md = q.to(dev), k.to(dev), v.to(dev), mask.to(dev)
+    out = torch.empty_like(qd)
+    lse = torch.empty(w.B, w.Hq, w.N, dtype=torch.float32, device=dev)
+    scale = w.softmax_scale()
+
+    def step():
+        st = fa.fwd_blocksparse_raw(qd, kd, vd, out, lse, md, w.causal, (-1, -1), scale)
+        if st != 0:
+            raise fa.FaError(st, fa.status_str(st))
+
+    def dense_step():
+        st = fa.fwd_raw(qd, kd, vd, out, lse, w.causal, (-1, -1), scale)
+        if st != 0:
+            raise fa.FaError(st, fa.status_str(st))
+
+    stream = torch.cuda.current_stream(dev)
+    ms_per_step, avg_s, med_s = timed(step, args, stream)
+    dense_ms, dense_avg, _ = timed(dense_step, args, stream)
+    pairs = sparse_pairs(w, mask)
+    pairs_total = sum(pairs[0 if len(pairs) == 1 else h] for h in range(w.Hq)) * w.B
+    flops = 4.0 * w.D * pairs_total
+    peak = PEAK_TFLOPS[w.dtype]
+    dense_flops = 4.0 * w.B * w.Hq * w.N * w.N * w.D / (2 if w.causal else 1)
+    rec = {
+        "metric": "block-sparse attention fwd TFLOP/s (4·D per admitted pair) and speedup over the dense causal pass",
+        "value": round(flops / (ms_per_step / 1e3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "N": w.N, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "causal": w.causal,
+                   "mask_heads": w.mask_heads, "band_blocks": w.band, "sink_blocks": w.sinks, "p_random": w.p_random,
+                   "block_density": round(float(mask.float().mean()), 5), "admitted_pairs": pairs_total,
+                   "softmax_scale": scale, "metric_flops": flops},
+        "pct_of_mfma_peak": round(100.0 * flops / (ms_per_step / 1e3) / 1e12 / peak, 2),
+        "dense_causal": {"ms_per_step": round(dense_ms, 5), "TFLOPs": round(dense_flops / (dense_ms / 1e3) / 1e12, 2),
+                         "speedup_of_sparse": round(dense_ms / ms_per_step, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(flops / avg_s / 1e12, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(flops / avg_s / 1e12 / peak, 4), "traffic": committed_traffic(w.name),
+                     "kernel_avg_us": round(avg_s * 1e6, 3), "kernel_median_us": round(med_s * 1e6, 3)},
+    }
+    if args.cpu_baseline_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline_sparse(w, q, k, v, mask, args.cpu_baseline_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline_sparse(w, q, k, v, mask, budget_s):
+    """The block-sparse oracle on the last rows of the sequence (whole heads of those rows), growing
+    the sample while it stays within budget_s; TFLOP/s on the admitted pairs it processed."""
+    import numpy as np
+    import torch
+
+    from oracle import admitted, attention_blocksparse_fp64, block_admitted, decode_bf16_bits, decode_f16_bits
+
+    def dec(x):
+        x = x.contiguous()
+        if x.dtype == torch.float16:
+            return decode_f16_bits(x.view(torch.int16).numpy().view(np.uint16))
+        return decode_bf16_bits(x.view(torch.int16).numpy().view(np.uint16))
+
+    G = w.Hq // w.Hkv
+    R = 128
+    done_flops, elapsed, heads = 0.0, 0.0, 0
+    t0 = time.perf_counter()
+    rows = np.arange(w.N - R, w.N)
+    for h in range(w.Hq):
+        g = h // G
+        bm = mask[0 if mask.shape[0] == 1 else h].numpy()
+        # the last R rows as a problem of Nq = R against all N keys (bottom-right alignment keeps the
+        # causal mask); their mask rows are the last R / 128 block rows
+        attention_blocksparse_fp64(dec(q[:, -R:, h:h + 1]), dec(k[:, :, g:g + 1]), dec(v[:, :, g:g + 1]),
+                                   bm[None, -(R // 128):], 128, 64, w.softmax_scale(), w.causal)
+        pairs = int((block_admitted(bm, w.N, w.N, 128, 64, rows=rows) & admitted(w.N, w.N, w.causal, rows=rows)).sum())
+        done_flops += 4.0 * w.D * pairs * w.B
+        heads += 1
+        elapsed = time.perf_counter() - t0
+        if elapsed >= budget_s:
+            break
+    threads, blas_name = blas_threads()
+    return {"value": done_flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"the last {R} rows of {heads} of {w.Hq} heads (all their keys), fp64, {elapsed:.1f} s wall; "
+                      f"admitted-pair FLOPs of those rows / wall time; BLAS={blas_name} threads={threads}, "
+                      f"host logical CPUs={os.cpu_count()}"}
 
 
 def kvcache_flops(w, lengths):
