@@ -23,7 +23,7 @@ A K/V head read by several query heads (MQA/GQA, reading R5 of ``oracle.attentio
 sum of their contributions: dk and dv of K/V head g add up the terms of every query head h with
 h // (Hq / Hkv) == g.
 
-Readings taken where the pages leave a point open (listed in the design doc as well):
+Readings taken where the pages leave a point open:
   RB1 The gradient is of the exact function (fp64 softmax of the fp64 scores of the given inputs);
       the kernel's own intermediate roundings (its fp16/bf16 out, the P operand of its products)
       are the kernel's error, measured against this.

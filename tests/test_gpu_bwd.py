@@ -1,6 +1,6 @@
 """GPU parity of the backward pass (fa_bwd, through the C ABI) against the fp64 gradient oracle.
 
-Bars (the pages and SURVEY give none for the backward pass; derived from the arithmetic): the
+Bars (the pages give none for the backward pass; derived from the arithmetic): the
 kernels round P and dS to the storage type for their products and round dq, dk, dv once on
 output, so each gradient is within a few units of that type's rounding of its own scale. With
 u = 2^-11 (fp16) or 2^-8 (bf16), per tensor:
