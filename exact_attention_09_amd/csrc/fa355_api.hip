@@ -100,9 +100,11 @@ namespace {
 
 // Key splits of fa_fwd_kvcache: enough waves to cover the chip several times over (one wave per
 // (batch, K/V head, row block, split)), splits of kDecMinKeys to kDecMaxKeys keys, a multiple of 32
-// (the upper bound keeps a split's page ids within a few KB of LDS).
-constexpr int64_t kDecTargetWaves = 4096;
-constexpr int kDecMinKeys = 256;
+// (the lower bound keeps a wave's fixed costs small against its streaming, the upper bound keeps a
+// split's page ids within a few KB of LDS). Measured on 128 sequences of 512-8192 keys (1024
+// pairs: 1024-key splits) and on 16 sequences of 4096-16384 keys (128 pairs: 512-key splits).
+constexpr int64_t kDecTargetWaves = 8192;
+constexpr int kDecMinKeys = 512;
 constexpr int kDecMaxKeys = 4096;
 void dec_split(int B, int Hkv, int row_blocks, int max_seqlen_k, int* n_split, int* split_keys) {
   const int64_t base = (int64_t)B * Hkv * row_blocks;

@@ -10,7 +10,7 @@
 // K and V rows with 64-bit per-lane addresses (each key may sit in another page), computes
 // S^T = K Q^T with K as the A operand straight from registers, runs the online softmax in its
 // registers (one query row per lane pair), and adds V^T P^T with V^T read transposed from its
-// own LDS tile. The next block's K and V are in flight during the current one. Each split writes
+// own LDS tile. The next two blocks' K and V are in flight during the current one. Each split writes
 // its normalised output and lse; fa_decode_merge_kernel combines the splits (or, with one split,
 // the wave writes the result itself).
 #include <hip/hip_runtime.h>
@@ -50,9 +50,20 @@ __global__ void __launch_bounds__(64) fa_decode_kernel(DecArgs a) {
   // past 256 registers, to one wave per SIMD; one buffer fewer measured slower all the same)
   constexpr int NB = 3;
   const int lane = threadIdx.x, hl = lane >> 5, l32 = lane & 31;
-  int u = blockIdx.x;
-  const int s = u % a.n_split;
-  u /= a.n_split;
+  // Which (pair, split): pair = (b * Hkv + hk) * row_blocks + rb. Workgroups are dealt
+  // round-robin to the 8 XCDs. With few splits per pair, consecutive ids take the same split of
+  // consecutive pairs (split-major): split-fastest ids would put split s on the XCDs congruent to
+  // s, and the first splits are the fullest. With many splits, the splits of a pair are
+  // consecutive (each XCD then meets every split index).
+  const int pairs = a.B * a.Hkv * a.row_blocks;
+  int s, u;
+  if (a.n_split < 16) {
+    s = (int)blockIdx.x / pairs;
+    u = (int)blockIdx.x - s * pairs;
+  } else {
+    s = (int)blockIdx.x % a.n_split;
+    u = (int)blockIdx.x / a.n_split;
+  }
   const int rb = u % a.row_blocks;
   u /= a.row_blocks;
   const int hk = u % a.Hkv, b = u / a.Hkv;
@@ -200,25 +211,33 @@ __global__ void __launch_bounds__(64) fa_decode_kernel(DecArgs a) {
     }
   };
 
-  // NB register buffers per trip, each in a fixed role: no register copies between blocks
+  // NB register buffers per trip, each in a fixed role: no register copies between blocks. The
+  // loop runs whole trips of NB blocks and the last blocks after it: with no exit from the middle
+  // of a trip (and no path into the loop that skips the first loads), the back edge is the only
+  // way back to the top, and the compiler's wait counts keep NB - 1 blocks in flight (an exit in
+  // mid-trip made it wait for every load at the top of each trip).
   i32x4 k0[KS], v0[KS], k1[KS], v1[KS], k2[KS], v2[KS];
   if (nblk > 0) {
     load_block(0, k0, v0);
-    if constexpr (NB == 3) load_block(1, k1, v1);
-  }
-  if constexpr (NB == 3) {
-    for (int n = 0; n < nblk; n += 3) {
-      step(n, k0, v0, k2, v2);
-      if (n + 1 >= nblk) break;
-      step(n + 1, k1, v1, k0, v0);
-      if (n + 2 >= nblk) break;
-      step(n + 2, k2, v2, k1, v1);
-    }
-  } else {
-    for (int n = 0; n < nblk; n += 2) {
-      step(n, k0, v0, k1, v1);
-      if (n + 1 >= nblk) break;
-      step(n + 1, k1, v1, k0, v0);
+    if constexpr (NB == 3) {
+      load_block(1, k1, v1);
+      int n = 0;
+      for (; n + 3 <= nblk; n += 3) {
+        step(n, k0, v0, k2, v2);
+        step(n + 1, k1, v1, k0, v0);
+        step(n + 2, k2, v2, k1, v1);
+      }
+      if (n < nblk) {
+        step(n, k0, v0, k2, v2);
+        if (n + 1 < nblk) step(n + 1, k1, v1, k0, v0);
+      }
+    } else {
+      int n = 0;
+      for (; n + 2 <= nblk; n += 2) {
+        step(n, k0, v0, k1, v1);
+        step(n + 1, k1, v1, k0, v0);
+      }
+      if (n < nblk) step(n, k0, v0, k1, v1);
     }
   }
 
