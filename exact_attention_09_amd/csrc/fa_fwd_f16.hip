@@ -349,7 +349,8 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
       }
       // Operand of MFMA e of the sequence (even e: S, K from LDS; odd e: PV, V^T from LDS), read
       // PF MFMAs ahead of its use. At D = 64 every read is issued up front (registers allow it
-      // and it measured fastest); at D = 128 a short distance keeps the kernel within 256
+      // and it measured fastest) and each MFMA waits only for its own operand (the compiler's
+      // per-use waits); at D = 128 a short distance keeps the kernel within 256
       // registers, so two waves share each SIMD.
       const uint32_t kslot = kring_a + r1, vslot = vring_a + r2;   // K(j+1), V(j-1)
       uint32_t kbase[KS], vbase[DB];
@@ -375,7 +376,6 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
       float rs = 0.f;
 #pragma unroll
       for (int e = 0; e < PF; ++e) read_operand(e);
-      if constexpr (PF == NM) __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
       // The sequence runs at raised issue priority: when both waves of a SIMD are ready, the one
       // inside its sequence (which feeds both pipes) issues first.
       __builtin_amdgcn_s_setprio(1);
