@@ -33,6 +33,10 @@ CASES = [
     (1, 2, 4, 4, 128, [2048], 0, True, (100, -1), "bf16"),           # dense cache, window
     (3, 1, 4, 2, 64, [31, 32, 33], 0, False, (-1, -1), "f16"),       # block edges, one split
     (2, 3, 6, 3, 128, [777, 2500], 1, True, (-1, -1), "f16"),        # one-token pages
+    # 16 or more splits per (sequence, K/V head) switch the launch order from split-major to
+    # consecutive splits of one pair (every case above has fewer)
+    (2, 1, 8, 2, 64, [9000, 4100], 16, False, (-1, -1), "bf16"),     # 18 splits of 512 keys
+    (1, 3, 8, 4, 128, [12000], 0, True, (-1, -1), "f16"),            # dense cache, 24 splits
 ]
 
 
