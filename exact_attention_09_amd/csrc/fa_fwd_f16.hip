@@ -22,9 +22,9 @@
 //    permuted key order with ds_read_b64_tr_b16 (LDS transpose read), so P never leaves
 //    registers.
 //  * K and V tiles (BN keys) stream HBM -> LDS with 128-bit buffer loads that write LDS directly
-//    (no register staging), into three-slot rings: while tile t is computed, the loads of K(t+3)
-//    and V(t+2) are in flight, so each load has two iterations to land. Each lane's 16 bytes land
-//    at its own slot position; which global chunk a lane fetches implements the LDS swizzle.
+//    (no register staging), into three-slot rings: step j issues the loads of K(j+3) and V(j+1),
+//    first read in step j+2, so each load has two steps to land. Each lane's 16 bytes land at its
+//    own slot position; which global chunk a lane fetches implements the LDS swizzle.
 //  * S of tile t+1 is computed while tile t goes through the softmax and the PV product (K runs
 //    one tile ahead of V), so the MFMAs of one overlap the VALU work of the other.
 //  * Softmax in base 2: t = s * (scale * log2 e); p = exp2(t - m); alpha = exp2(m_old - m_new).
