@@ -27,10 +27,13 @@ after one forward pass that provides out and lse) on the same workload; its FLOP
 2.5 times the forward's (the five products of the method's backward pass).
 
 Also reported:
-  * roofline — the kernel's achieved TFLOP/s against MI355X's dense MFMA peak for its dtype,
-    from HIP events recorded around each launch on the launch stream (mean and median per
-    launch); HBM traffic from the committed rocprofv3 counter summary when it was taken on the
-    current kernel source;
+  * roofline — the kernel's achieved TFLOP/s against MI355X's dense MFMA peak for its dtype, from
+    two HIP events on the launch stream around the K timed launches (the mean launch; the median
+    comes from K further launches each between two events); HBM traffic from the committed
+    rocprofv3 counter summary when it was taken on the current kernel source;
+  * timing — the protocol (see `timed`): W warm-up steps, K steps as a run from an idle GPU sees
+    them (`unheated_ms_per_step`), the step repeated for a quarter of a second (the engine clock
+    rises over the first tenths of a second under load), then the K timed steps;
   * cold_cache — the median launch after 512 MiB of writes have evicted L2 and the MALL;
   * cpu_baseline — the fp64 CPU oracle timed on this host on a bounded sample of the same
     workload (whole heads), scaled to the same metric.
@@ -288,25 +291,8 @@ def main():
             if st != 0:
                 raise fa.FaError(st, fa.status_str(st))
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
     stream = torch.cuda.current_stream(dev)     # fa_fwd launches on this stream
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    avg_kernel_s = sum(kernel_ms) / len(kernel_ms) / 1e3
-    med_kernel_s = sorted(kernel_ms)[len(kernel_ms) // 2] / 1e3
-    ms_per_step = wall / args.steps * 1e3
+    ms_per_step, avg_kernel_s, med_kernel_s, tinfo = timed(step, args, stream)
 
     # Cold-cache variant: 512 MiB written between launches evicts L2 and the MALL.
     cold = None
@@ -357,6 +343,7 @@ def main():
                      "algorithmic_bytes": alg_bytes,
                      "algorithmic_GBps": round(alg_bytes / avg_kernel_s / 1e9, 1)},
     }
+    rec["timing"] = tinfo
     if cold is not None:
         rec["cold_cache"] = cold
     if bwd:
@@ -367,25 +354,55 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
+PREHEAT_S = 0.25   # seconds of the step run before the timed region (engine clock ramp)
+
+
 def timed(step, args, stream):
-    """Warm-up, then args.steps launches bracketed by HIP events on the launch stream; returns
-    (ms_per_step by wall clock, mean launch s, median launch s)."""
+    """The timing protocol of every bench line. W warm-up steps; K steps as a run that starts on an
+    idle GPU sees them (reported as `unheated_ms_per_step`, not the value); the step repeated for
+    PREHEAT_S seconds, because the engine clock rises over the first few tenths of a second under
+    load (measured: c3 366-372 us per launch right after 10 warm-ups, 346 after a pre-heat; c5
+    160 vs 137); then the K timed steps, back to back between a synchronize on each side (wall
+    clock: `ms_per_step`, the value) with two HIP events on the launch stream around them (the mean
+    launch); then K more launches, each between two events (the median launch). Returns
+    (ms_per_step, mean launch s, median launch s, info)."""
     import torch
+
+    def back_to_back(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(n):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, e0.elapsed_time(e1) / 1e3
+
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    _, unheated_s = back_to_back(args.steps)
+    pre = 0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    while time.perf_counter() - t0 < PREHEAT_S:
+        for _ in range(4):
+            step()
+        pre += 4
+        torch.cuda.synchronize()
+    wall, events_s = back_to_back(args.steps)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     for i in range(args.steps):
         starts[i].record(stream)
         step()
         ends[i].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return wall / args.steps * 1e3, sum(ms) / len(ms) / 1e3, sorted(ms)[len(ms) // 2] / 1e3
+    ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    info = {"preheat_s": PREHEAT_S, "preheat_launches": pre,
+            "unheated_ms_per_step": round(unheated_s / args.steps * 1e3, 5),
+            "order": "warmup, unheated steps, preheat, timed steps, per-launch steps"}
+    return wall / args.steps * 1e3, events_s / args.steps, ms[len(ms) // 2] / 1e3, info
 
 
 def bench_varlen(args, w, dev):
@@ -408,7 +425,7 @@ def bench_varlen(args, w, dev):
         if st != 0:
             raise fa.FaError(st, fa.status_str(st))
 
-    ms_per_step, avg_s, med_s = timed(step, args, torch.cuda.current_stream(dev))
+    ms_per_step, avg_s, med_s, tinfo = timed(step, args, torch.cuda.current_stream(dev))
     flops = varlen_flops(w, lengths)
     peak = PEAK_TFLOPS[w.dtype]
     es = 1 if w.dtype == "e4m3" else 2
@@ -425,6 +442,7 @@ def bench_varlen(args, w, dev):
                      "frac": round(flops / avg_s / 1e12 / peak, 4), "traffic": committed_traffic(w.name),
                      "kernel_avg_us": round(avg_s * 1e6, 3), "kernel_median_us": round(med_s * 1e6, 3),
                      "algorithmic_bytes": alg_bytes, "algorithmic_GBps": round(alg_bytes / avg_s / 1e9, 1)},
+        "timing": tinfo,
     }
     if args.cpu_baseline_seconds > 0:
         rec["cpu_baseline"] = cpu_baseline_varlen(w, lengths, q, k, v, cu_q, descale, args.cpu_baseline_seconds)
@@ -476,8 +494,8 @@ def bench_sparse(args, w, dev):
             raise fa.FaError(st, fa.status_str(st))
 
     stream = torch.cuda.current_stream(dev)
-    ms_per_step, avg_s, med_s = timed(step, args, stream)
-    dense_ms, dense_avg, _ = timed(dense_step, args, stream)
+    ms_per_step, avg_s, med_s, tinfo = timed(step, args, stream)
+    dense_ms, dense_avg, _, dinfo = timed(dense_step, args, stream)
     pairs = sparse_pairs(w, mask)
     pairs_total = sum(pairs[0 if len(pairs) == 1 else h] for h in range(w.Hq)) * w.B
     flops = 4.0 * w.D * pairs_total
@@ -494,10 +512,11 @@ def bench_sparse(args, w, dev):
                    "softmax_scale": scale, "metric_flops": flops},
         "pct_of_mfma_peak": round(100.0 * flops / (ms_per_step / 1e3) / 1e12 / peak, 2),
         "dense_causal": {"ms_per_step": round(dense_ms, 5), "TFLOPs": round(dense_flops / (dense_ms / 1e3) / 1e12, 2),
-                         "speedup_of_sparse": round(dense_ms / ms_per_step, 2)},
+                         "speedup_of_sparse": round(dense_ms / ms_per_step, 2), "timing": dinfo},
         "roofline": {"bound": "mfma", "achieved": round(flops / avg_s / 1e12, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(flops / avg_s / 1e12 / peak, 4), "traffic": committed_traffic(w.name),
                      "kernel_avg_us": round(avg_s * 1e6, 3), "kernel_median_us": round(med_s * 1e6, 3)},
+        "timing": tinfo,
     }
     if args.cpu_baseline_seconds > 0:
         rec["cpu_baseline"] = cpu_baseline_sparse(w, q, k, v, mask, args.cpu_baseline_seconds)
@@ -574,7 +593,7 @@ def bench_kvcache(args, w, dev):
         if st != 0:
             raise fa.FaError(st, fa.status_str(st))
 
-    ms_per_step, avg_s, med_s = timed(step, args, torch.cuda.current_stream(dev))
+    ms_per_step, avg_s, med_s, tinfo = timed(step, args, torch.cuda.current_stream(dev))
     flops = kvcache_flops(w, lengths)
     es = 2
     kv_bytes = 2 * sum(lengths) * w.Hkv * w.D * es
@@ -593,6 +612,7 @@ def bench_kvcache(args, w, dev):
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": committed_traffic(w.name, "decode"),
                      "kernel_avg_us": round(avg_s * 1e6, 3), "kernel_median_us": round(med_s * 1e6, 3),
                      "algorithmic_bytes": alg_bytes},
+        "timing": tinfo,
     }
     if args.cpu_baseline_seconds > 0:
         rec["cpu_baseline"] = cpu_baseline_kvcache(w, lengths, q, k, v, table, args.cpu_baseline_seconds, alg_bytes)
