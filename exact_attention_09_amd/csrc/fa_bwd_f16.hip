@@ -19,9 +19,12 @@
 //    query head that reads this K/V head) that attend to its keys. Lanes own keys: S = Q K^T and
 //    dP = dO V^T come out with one key per lane; P and dS are the B operands of
 //    dV^T = dO^T P and dK^T = Q^T dS, with dO^T and Q^T read by transpose reads.
-// Tiles stream HBM -> LDS by 128-bit LDS-direct loads into two-slot rings; every tile uses the
-// row swizzle of the forward kernel's K tile (conflict-free row reads); transpose reads pick the
-// swizzle of each 8-row group.
+// Tiles stream HBM -> LDS by 128-bit LDS-direct loads into rings of three slots (two for the
+// dq kernel at D = 128, where a third would leave room for one workgroup per CU instead of two):
+// a step's loads are issued right after its barrier into the slot freed by the step before, so
+// they have the rest of the ring to land, and one barrier per step both publishes the landed
+// tile and frees the next slot. Every tile uses the row swizzle of the forward kernel's K tile
+// (conflict-free row reads); transpose reads pick the swizzle of each 8-row group.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -90,9 +93,10 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(BwdArgs a) {
   constexpr int NT = 256, BM = kBwdQRows, BN = 64, ES = 2;
   constexpr int ROWB = T::ROWB, TILEB = T::TILEB, KS = T::KS, DB = T::DB, KB = BN / 32;
   constexpr int CH = BN * (D / 8) / NT;     // 16-byte loads per thread per tile
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILEB];   // [K0 K1 | V0 V1]
+  constexpr int NSL = D == 64 ? 3 : 2;      // ring slots per tensor
+  __shared__ __attribute__((aligned(16))) char smem[2 * NSL * TILEB];   // [K ring | V ring]
   char* const kring = smem;
-  char* const vring = smem + 2 * TILEB;
+  char* const vring = smem + NSL * TILEB;
 
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -175,18 +179,21 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) dq[db] = f32x16{};
 
-  if (tb < te) {
-    dma(k_d, kgoff, (uint32_t)(tb * BN) * k_rowb, kring_a);
-    dma(v_d, vgoff, (uint32_t)(tb * BN) * v_rowb, vring_a);
-  }
-  for (int t = tb; t < te; ++t) {
-    const uint32_t s = (uint32_t)((t - tb) & 1) * TILEB;
-    const bool more = t + 1 < te;
-    if (more) {
-      dma(k_d, kgoff, (uint32_t)((t + 1) * BN) * k_rowb, kring_a + (TILEB - s));
-      dma(v_d, vgoff, (uint32_t)((t + 1) * BN) * v_rowb, vring_a + (TILEB - s));
+#pragma unroll
+  for (int i = 0; i < NSL - 1; ++i)
+    if (tb + i < te) {
+      dma(k_d, kgoff, (uint32_t)((tb + i) * BN) * k_rowb, kring_a + i * TILEB);
+      dma(v_d, vgoff, (uint32_t)((tb + i) * BN) * v_rowb, vring_a + i * TILEB);
     }
-    barrier_keep(more ? 2 * CH : 0);   // tile t landed for every wave
+  uint32_t s = 0, sn = (NSL - 1) * TILEB;   // slots of tiles t and t + NSL - 1
+  for (int t = tb; t < te; ++t) {
+    // tile t landed (with three slots, tile t + 1's loads stay in flight) and every wave is done
+    // with tile t - 1, whose slot tile t + NSL - 1 refills
+    barrier_keep(NSL == 3 && t + 1 < te ? 2 * CH : 0);
+    if (t + NSL - 1 < te) {
+      dma(k_d, kgoff, (uint32_t)((t + NSL - 1) * BN) * k_rowb, kring_a + sn);
+      dma(v_d, vgoff, (uint32_t)((t + NSL - 1) * BN) * v_rowb, vring_a + sn);
+    }
     const bool live = wave_live && t * BN + BN - 1 >= wlo0 && t * BN <= whi1;
     if (live) {
       uint32_t kt_base[DB][2];
@@ -235,7 +242,8 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(BwdArgs a) {
           for (int db = 0; db < DB; ++db) dq[db] = TR::mfma(tr_operand<D>(kt_base, kb, half, db), dsop, dq[db]);
         }
     }
-    barrier_keep(more ? 2 * CH : 0);   // every wave is done with slot s before it is refilled
+    sn = s;
+    s = s == (NSL - 1) * TILEB ? 0 : s + TILEB;
   }
 
   if (!wave_live || my_row >= a.Nq) return;
@@ -259,12 +267,12 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int ROWB = T::ROWB, TILEB = T::TILEB, KS = T::KS, DB = T::DB, QB = BQ / 32;
   constexpr int CH = BQ * (D / 8) / NT;
   constexpr int NS = 2 * KS, ND = 4 * DB;   // products per 32-query block: S and dP, dV and dK
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILEB];   // [Q0 Q1 | dO0 dO1]
+  __shared__ __attribute__((aligned(16))) char smem[6 * TILEB];   // [Q0 Q1 Q2 | dO0 dO1 dO2]
   char* const qring = smem;
-  char* const dring = smem + 2 * TILEB;
+  char* const dring = smem + 3 * TILEB;
   // -lse / scale and -delta of each slot's 64 query rows (1 KB per row set: the 4-byte LDS-direct
   // load of a wave covers 256 bytes, the rest is slack)
-  __shared__ __attribute__((aligned(16))) char sbuf[2 * 2 * 1024];
+  __shared__ __attribute__((aligned(16))) char sbuf[3 * 2 * 1024];
 
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -353,7 +361,7 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
     }
   };
   const uint32_t sbuf_a = lds_addr_of(sbuf);
-  // loads of the step (query head hh, query tile u) into ring slot `slot` (0 or TILEB): Q and dO
+  // loads of the step (query head hh, query tile u) into the ring slot at byte offset `slot`: Q and dO
   // tiles, and the tile's rows of both workspace halves (every wave loads those 64 values into
   // the same place: 2 loads, same count per wave)
   auto issue = [&](int hh, int u, uint32_t slot) {
@@ -364,7 +372,7 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
     const int64_t row0 = ((int64_t)b * a.Hq + hh) * a.Nq;
     const BufDesc w_d = make_desc(a.delta + (int64_t)a.B * a.Hq * a.Nq + row0, (uint32_t)a.Nq * 4u);
     const BufDesc e_d = make_desc(a.delta + row0, (uint32_t)a.Nq * 4u);
-    const uint32_t st = sbuf_a + (slot ? 2048u : 0u);
+    const uint32_t st = sbuf_a + (slot / TILEB) * 2048u;
     dma4(w_d, lane * 4, (uint32_t)(u * BQ) * 4u, st);
     dma4(e_d, lane * 4, (uint32_t)(u * BQ) * 4u, st + 1024);
   };
@@ -419,15 +427,21 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
     issue(next_h, next_u, 0);
     advance(next_h, next_u);
   }
+  if (nsteps > 1) {
+    issue(next_h, next_u, TILEB);
+    advance(next_h, next_u);
+  }
+  uint32_t s = 0, s2 = 2 * TILEB;            // slots of steps n and n + 2
   for (int n = 0; n < nsteps; ++n) {
-    const uint32_t s = (uint32_t)(n & 1) * TILEB;
     const bool more = n + 1 < nsteps;
-    if (more) {
-      issue(next_h, next_u, TILEB - s);
+    // step n's loads landed (step n + 1's stay in flight) and every wave is done with step n - 1,
+    // whose slot step n + 2 refills
+    barrier_keep(more);
+    if (n + 2 < nsteps) {
+      issue(next_h, next_u, s2);
       advance(next_h, next_u);
     }
-    barrier_keep(more);
-    const uint32_t st = sbuf_a + (s ? 2048u : 0u);
+    const uint32_t st = sbuf_a + (s / TILEB) * 2048u;
     uint32_t qt_base[DB][2], dt_base[DB][2], qr[KS], dr[KS];
     tr_bases<D>(qring_a + s, toff, qt_base);
     tr_bases<D>(dring_a + s, toff, dt_base);
@@ -546,8 +560,9 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
         for (int m = 0; m < ND; ++m) dvdk_mfma(m, dvdk_operand(qb, m), pk, dsk);
       }
     }
-    barrier_keep(more);
     if (++u == ue) u = ub;
+    s2 = s;
+    s = s == 2 * TILEB ? 0 : s + TILEB;
   }
 
   if (my_key >= a.Nk) return;
