@@ -13,24 +13,34 @@
 #include "fa_mask.hpp"
 
 namespace fa {
-hipError_t launch_fwd_f16(const FwdArgs& a, int D, int dtype, int64_t grid, hipStream_t stream);
+hipError_t launch_fwd_f16(const FwdArgs& a, int D, int dtype, int block_n, int64_t grid, hipStream_t stream);
 hipError_t launch_fwd_fp8(const FwdArgs& a, int D, int64_t grid, hipStream_t stream);
 
-TileShape tile_shape(int D, int dtype) {
+bool short_rows(int D, int dtype, int causal, int wl, int wr, bool sparse) {
+  if (D != 128 || dtype == FA_FP8_E4M3 || sparse || wl < 0) return false;
+  const int right = causal ? 0 : wr;
+  return right >= 0 && (int64_t)wl + right + 1 <= kShortRowKeys;
+}
+
+TileShape tile_shape(int D, int dtype, bool few_keys) {
   TileShape t;
-  // fp16/bf16 at D = 128: 8 waves (two per SIMD, the register budget allows no more); otherwise
-  // 4 waves, two workgroups per compute unit
-  t.waves = (dtype != FA_FP8_E4M3 && D == 128) ? 8 : 4;
+  // fp16/bf16 at D = 128: 8 waves (two per SIMD, the register budget allows no more) and 64-key
+  // tiles, one workgroup per compute unit. Rows that admit few keys (a window) make short
+  // workgroups whose pipeline start and end dominate; there, 4 waves with 32-key tiles (half the
+  // LDS) let two workgroups share a compute unit and overlap. Otherwise 4 waves and 64-key
+  // tiles, two workgroups per compute unit.
+  const bool wide = dtype != FA_FP8_E4M3 && D == 128 && !few_keys;
+  t.waves = wide ? 8 : 4;
   t.block_m = 32 * t.waves;
-  t.block_n = 64;
+  t.block_n = (D == 128 && few_keys && dtype != FA_FP8_E4M3) ? 32 : 64;
   const int es = dtype == FA_FP8_E4M3 ? 1 : 2;
   t.lds_bytes = (3 + 3) * t.block_n * D * es;   // three-slot K and V rings
   return t;
 }
 
-hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, int64_t grid, hipStream_t stream) {
+hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, int block_n, int64_t grid, hipStream_t stream) {
   if (dtype == FA_FP8_E4M3) return launch_fwd_fp8(a, D, grid, stream);
-  return launch_fwd_f16(a, D, dtype, grid, stream);
+  return launch_fwd_f16(a, D, dtype, block_n, grid, stream);
 }
 }  // namespace fa
 
@@ -51,8 +61,7 @@ fa_status check_sizes(int B, int Nq, int Nk, int Hq, int Hkv, int D, int wl, int
   if (Nq > kMaxSeq || Nk > kMaxSeq || Hq % Hkv != 0) return FA_ERR_SHAPE;
   if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
   if (wl < -1 || wr < -1) return FA_ERR_WINDOW;
-  const fa::TileShape ts = fa::tile_shape(D, dtype);
-  const int64_t tiles = ((int64_t)Nq + ts.block_m - 1) / ts.block_m;
+  const int64_t tiles = ((int64_t)Nq + 127) / 128;   // 128 rows: the smallest query tile
   if ((int64_t)B * Hq * tiles >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
   return FA_OK;
 }
@@ -187,7 +196,8 @@ fa_status fa_fwd_plan(int B, int Nq, int Nk, int Hq, int Hkv, int D, int causal,
   if (!info) return FA_ERR_NULL;
   const fa_status st = check_sizes(B, Nq, Nk, Hq, Hkv, D, window_left, window_right, dtype);
   if (st != FA_OK) return st;
-  const fa::TileShape ts = fa::tile_shape(D, dtype);
+  const fa::TileShape ts =
+      fa::tile_shape(D, dtype, fa::short_rows(D, dtype, causal, window_left, window_right, false));
   info->block_m = ts.block_m;
   info->block_n = ts.block_n;
   info->waves = ts.waves;
@@ -270,10 +280,11 @@ fa_status fwd_impl(const void* q, const void* k, const void* v, void* out, float
   a.mask_heads = mask_heads;
   a.nqb = (Nq + fa::kSparseBlockQ - 1) / fa::kSparseBlockQ;
   a.nkb = (Nk + fa::kSparseBlockK - 1) / fa::kSparseBlockK;
-  const fa::TileShape ts = fa::tile_shape(D, dtype);
+  const fa::TileShape ts =
+      fa::tile_shape(D, dtype, fa::short_rows(D, dtype, causal, window_left, window_right, block_mask != nullptr));
   a.num_q_tiles = (Nq + ts.block_m - 1) / ts.block_m;
   const int64_t grid = (int64_t)B * Hq * a.num_q_tiles;
-  const hipError_t e = fa::launch_fwd(a, D, dtype, grid, stream);
+  const hipError_t e = fa::launch_fwd(a, D, dtype, ts.block_n, grid, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -363,10 +374,10 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, 
   a.mask_heads = a.nqb = a.nkb = 0;
   a.total_q = total_q;
   a.total_k = total_k;
-  const fa::TileShape ts = fa::tile_shape(D, dtype);
+  const fa::TileShape ts = fa::tile_shape(D, dtype, fa::short_rows(D, dtype, causal, window_left, window_right, false));
   a.num_q_tiles = (max_seqlen_q + ts.block_m - 1) / ts.block_m;
   const int64_t grid = (int64_t)B * Hq * a.num_q_tiles;
-  const hipError_t e = fa::launch_fwd(a, D, dtype, grid, stream);
+  const hipError_t e = fa::launch_fwd(a, D, dtype, ts.block_n, grid, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

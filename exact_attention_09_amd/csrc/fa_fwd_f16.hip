@@ -436,20 +436,23 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
 }
 
 template <class TR, int D>
-static hipError_t launch_t(const FwdArgs& a, int64_t grid, hipStream_t stream) {
+static hipError_t launch_t(const FwdArgs& a, int block_n, int64_t grid, hipStream_t stream) {
   constexpr int BN = 64, WAVES = D == 64 ? 4 : 8;
   static_assert(BN == kSparseBlockK && (WAVES * 32) % kSparseBlockQ == 0, "tiles nest in the mask's blocks");
   if (a.block_mask != nullptr)
     hipLaunchKernelGGL((fa_fwd_kernel<TR, D, BN, WAVES, true>), dim3((unsigned)grid), dim3(WAVES * 64),
                        (size_t)(2 * a.nkb + 1) * 4, stream, a);
+  else if (D == 128 && block_n == 32)   // rows with few keys: 4 waves, 32-key tiles
+    hipLaunchKernelGGL((fa_fwd_kernel<TR, D, 32, 4, false>), dim3((unsigned)grid), dim3(4 * 64), 0, stream, a);
   else
     hipLaunchKernelGGL((fa_fwd_kernel<TR, D, BN, WAVES, false>), dim3((unsigned)grid), dim3(WAVES * 64), 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_f16(const FwdArgs& a, int D, int dtype, int64_t grid, hipStream_t stream) {
-  if (dtype == 0) return D == 64 ? launch_t<F16, 64>(a, grid, stream) : launch_t<F16, 128>(a, grid, stream);
-  return D == 64 ? launch_t<BF16, 64>(a, grid, stream) : launch_t<BF16, 128>(a, grid, stream);
+hipError_t launch_fwd_f16(const FwdArgs& a, int D, int dtype, int block_n, int64_t grid, hipStream_t stream) {
+  if (dtype == 0)
+    return D == 64 ? launch_t<F16, 64>(a, block_n, grid, stream) : launch_t<F16, 128>(a, block_n, grid, stream);
+  return D == 64 ? launch_t<BF16, 64>(a, block_n, grid, stream) : launch_t<BF16, 128>(a, block_n, grid, stream);
 }
 
 }  // namespace fa

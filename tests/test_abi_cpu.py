@@ -192,5 +192,44 @@ def test_plan(lib):
     # fp8: 4-wave kernel
     p = fa.plan(2, 4096, 4096, 32, 32, 64, causal=True, dtype=fa.FA_FP8_E4M3)
     assert p["block_m"] == 128 and p["grid"] == 2 * 32 * 32
+
+
+def _window_key_tiles(Nq, Nk, causal, window, block_m, block_n):
+    """Key tiles of block_n keys holding an admitted key of some row of each query tile of block_m
+    rows, by brute force over the admission rule (0 <= j < Nk, j <= i + off under the causal
+    mask, i + off - wl <= j <= i + off + wr for a window, off = Nk - Nq)."""
+    off = Nk - Nq
+    i = np.arange(Nq)[:, None]
+    j = np.arange(Nk)[None, :]
+    m = np.ones((Nq, Nk), bool)
+    if causal:
+        m &= j <= i + off
+    if window[0] >= 0:
+        m &= j >= i + off - window[0]
+    if window[1] >= 0:
+        m &= j <= i + off + window[1]
+    total = 0
+    for r0 in range(0, Nq, block_m):
+        cols = m[r0:r0 + block_m].any(0)
+        total += len(np.unique(np.nonzero(cols)[0] // block_n))
+    return total
+
+
+@pytest.mark.parametrize("causal,window,few", [(False, (100, 30), True), (True, (256, 256), True),
+                                               (True, (1023, -1), True), (True, (1024, -1), False),
+                                               (False, (1000, 100), False), (False, (100, -1), False)])
+def test_plan_few_keys_launch_shape(lib, causal, window, few):
+    # At D = 128 (fp16/bf16), rows that admit at most 1024 keys take 4-wave workgroups with 32-key
+    # tiles; other calls keep 8 waves and 64-key tiles. D = 64 and fp8 never change.
+    Nq, Nk = 1000, 1100
+    p = fa.plan(2, Nq, Nk, 4, 2, 128, causal=causal, window=window, dtype=fa.FA_BF16)
+    bm, bn = (128, 32) if few else (256, 64)
+    assert (p["block_m"], p["block_n"], p["waves"]) == (bm, bn, bm // 32)
+    assert p["lds_bytes"] == 6 * bn * 128 * 2
+    assert p["num_q_tiles"] == -(-Nq // bm) and p["grid"] == 2 * 4 * p["num_q_tiles"]
+    assert p["kv_tiles"] == 2 * 4 * _window_key_tiles(Nq, Nk, causal, window, bm, bn)
+    for D, dt in ((64, fa.FA_F16), (128, fa.FA_FP8_E4M3)):
+        q = fa.plan(2, Nq, Nk, 4, 2, D, causal=causal, window=window, dtype=dt)
+        assert (q["block_m"], q["block_n"], q["waves"]) == (128, 64, 4)
     with pytest.raises(fa.FaError):
         fa.plan(1, 128, 128, 3, 2, 64)
