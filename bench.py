@@ -27,8 +27,10 @@ after one forward pass that provides out and lse) on the same workload; its FLOP
 2.5 times the forward's (the five products of the method's backward pass).
 
 Also reported:
-  * roofline — the kernel's achieved TFLOP/s against MI355X's dense MFMA peak for its dtype, from
-    two HIP events on the launch stream around the K timed launches (the mean launch; the median
+  * roofline — against the roof that binds the workload: the MFMA peak for its dtype (TFLOP/s),
+    or HBM bandwidth (GB/s of algorithmic bytes) when those bytes take longer at 8 TB/s than the
+    FLOPs at the MFMA peak (the window workloads; the TFLOP/s figures stay beside it); the mean
+    launch from two HIP events on the launch stream around the K timed launches (the median
     comes from K further launches each between two events); HBM traffic from the committed
     rocprofv3 counter summary when it was taken on the current kernel source;
   * timing — the protocol (see `timed`): W warm-up steps, K steps as a run from an idle GPU sees
@@ -97,6 +99,12 @@ def varlen_flops(w, lengths):
         else:
             total += 4.0 * w.Hq * w.D * admitted_pairs(n, n, w.causal, w.window)
     return total
+
+
+def roofline_bound(flops, alg_bytes, peak_tflops):
+    """The roof that binds: "hbm" when the algorithmic bytes take longer at the HBM peak than the
+    FLOPs at the MFMA peak, else "mfma"."""
+    return "hbm" if alg_bytes / (HBM_PEAK_GBS * 1e9) > flops / (peak_tflops * 1e12) else "mfma"
 
 
 def algorithmic_bytes(w):
@@ -343,6 +351,11 @@ def main():
                      "algorithmic_bytes": alg_bytes,
                      "algorithmic_GBps": round(alg_bytes / avg_kernel_s / 1e9, 1)},
     }
+    if roofline_bound(flops, alg_bytes, peak) == "hbm":
+        gbs = alg_bytes / avg_kernel_s / 1e9
+        rec["roofline"].update({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(gbs / HBM_PEAK_GBS, 4), "achieved_TFLOPs": round(achieved, 2),
+                                "frac_of_mfma_peak": round(achieved / peak, 4)})
     rec["timing"] = tinfo
     if cold is not None:
         rec["cold_cache"] = cold

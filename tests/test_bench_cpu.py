@@ -97,3 +97,19 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     line = json.loads(r.stdout.strip().splitlines()[-1])
     assert "error" in line and line["n_gpus"] == 2
+
+
+def test_roofline_bound_of_the_workloads():
+    # the window workloads move more bytes at 8 TB/s than they compute at the MFMA peak; the
+    # causal and full workloads are the other way round
+    for name, w in WORKLOADS.items():
+        flops, nbytes = bench.metric_flops(w), bench.algorithmic_bytes(w)
+        want = "hbm" if w.window != (-1, -1) else "mfma"
+        if name.startswith("mha_"):   # the small parity cases (launch-bound in practice): 0.13 MB
+            want = "hbm"              # against 8 MFLOP, 4.2 MB against 1.07 GFLOP
+        assert bench.roofline_bound(flops, nbytes, bench.PEAK_TFLOPS[w.dtype]) == want, name
+    w = WORKLOADS["gqa_win256_b1_hq32_hkv8_n16384_d128_bf16"]
+    assert bench.algorithmic_bytes(w) == 337641472
+    assert bench.roofline_bound(bench.metric_flops(w), 337641472, 2516.6) == "hbm"
+    assert bench.roofline_bound(bench.metric_flops(w), 337641472, 1e9) == "hbm"
+    assert bench.roofline_bound(bench.metric_flops(w), 1, 2516.6) == "mfma"
