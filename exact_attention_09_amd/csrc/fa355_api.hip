@@ -17,7 +17,7 @@ hipError_t launch_fwd_f16(const FwdArgs& a, int D, int dtype, int block_n, int64
 hipError_t launch_fwd_fp8(const FwdArgs& a, int D, int64_t grid, hipStream_t stream);
 
 bool short_rows(int D, int dtype, int causal, int wl, int wr, bool sparse) {
-  if (D != 128 || dtype == FA_FP8_E4M3 || sparse || wl < 0) return false;
+  if (dtype == FA_FP8_E4M3 || sparse || wl < 0) return false;
   const int right = causal ? 0 : wr;
   return right >= 0 && (int64_t)wl + right + 1 <= kShortRowKeys;
 }
@@ -25,14 +25,15 @@ bool short_rows(int D, int dtype, int causal, int wl, int wr, bool sparse) {
 TileShape tile_shape(int D, int dtype, bool few_keys) {
   TileShape t;
   // fp16/bf16 at D = 128: 8 waves (two per SIMD, the register budget allows no more) and 64-key
-  // tiles, one workgroup per compute unit. Rows that admit few keys (a window) make short
-  // workgroups whose pipeline start and end dominate; there, 4 waves with 32-key tiles (half the
-  // LDS) let two workgroups share a compute unit and overlap. Otherwise 4 waves and 64-key
-  // tiles, two workgroups per compute unit.
+  // tiles, one workgroup per compute unit; otherwise 4 waves and 64-key tiles, two workgroups per
+  // compute unit. Rows that admit few keys (a window) make short workgroups whose pipeline start
+  // and end dominate; there, fp16/bf16 calls take 4 waves with 32-key tiles (half the LDS and
+  // fewer registers), so that more workgroups share a compute unit and overlap (two at D = 128,
+  // three at D = 64).
   const bool wide = dtype != FA_FP8_E4M3 && D == 128 && !few_keys;
   t.waves = wide ? 8 : 4;
   t.block_m = 32 * t.waves;
-  t.block_n = (D == 128 && few_keys && dtype != FA_FP8_E4M3) ? 32 : 64;
+  t.block_n = (few_keys && dtype != FA_FP8_E4M3) ? 32 : 64;
   const int es = dtype == FA_FP8_E4M3 ? 1 : 2;
   t.lds_bytes = (3 + 3) * t.block_n * D * es;   // three-slot K and V rings
   return t;

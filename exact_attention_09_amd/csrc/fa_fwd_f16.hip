@@ -442,7 +442,7 @@ static hipError_t launch_t(const FwdArgs& a, int block_n, int64_t grid, hipStrea
   if (a.block_mask != nullptr)
     hipLaunchKernelGGL((fa_fwd_kernel<TR, D, BN, WAVES, true>), dim3((unsigned)grid), dim3(WAVES * 64),
                        (size_t)(2 * a.nkb + 1) * 4, stream, a);
-  else if (D == 128 && block_n == 32)   // rows with few keys: 4 waves, 32-key tiles
+  else if (block_n == 32)   // rows with few keys: 4 waves, 32-key tiles
     hipLaunchKernelGGL((fa_fwd_kernel<TR, D, 32, 4, false>), dim3((unsigned)grid), dim3(4 * 64), 0, stream, a);
   else
     hipLaunchKernelGGL((fa_fwd_kernel<TR, D, BN, WAVES, false>), dim3((unsigned)grid), dim3(WAVES * 64), 0, stream, a);

@@ -139,9 +139,9 @@ struct TileShape {
   int block_m, block_n, waves, lds_bytes;
 };
 
-// Whether a fp16/bf16 call at D = 128 takes the few-keys launch shape (4-wave workgroups, 32-key
-// tiles): every row admits at most kShortRowKeys keys (a window) and the call is dense or packed,
-// not block-sparse.
+// Whether a fp16/bf16 call takes the few-keys launch shape (4-wave workgroups, 32-key tiles):
+// every row admits at most kShortRowKeys keys (a window) and the call is dense or packed, not
+// block-sparse.
 constexpr int kShortRowKeys = 1024;
 bool short_rows(int D, int dtype, int causal, int wl, int wr, bool sparse);
 TileShape tile_shape(int D, int dtype, bool few_keys);

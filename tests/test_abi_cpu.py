@@ -219,8 +219,8 @@ def _window_key_tiles(Nq, Nk, causal, window, block_m, block_n):
                                                (True, (1023, -1), True), (True, (1024, -1), False),
                                                (False, (1000, 100), False), (False, (100, -1), False)])
 def test_plan_few_keys_launch_shape(lib, causal, window, few):
-    # At D = 128 (fp16/bf16), rows that admit at most 1024 keys take 4-wave workgroups with 32-key
-    # tiles; other calls keep 8 waves and 64-key tiles. D = 64 and fp8 never change.
+    # fp16/bf16 calls whose rows admit at most 1024 keys take 4-wave workgroups with 32-key tiles;
+    # other calls keep 64-key tiles (8 waves at D = 128, 4 at D = 64). fp8 never changes.
     Nq, Nk = 1000, 1100
     p = fa.plan(2, Nq, Nk, 4, 2, 128, causal=causal, window=window, dtype=fa.FA_BF16)
     bm, bn = (128, 32) if few else (256, 64)
@@ -228,8 +228,11 @@ def test_plan_few_keys_launch_shape(lib, causal, window, few):
     assert p["lds_bytes"] == 6 * bn * 128 * 2
     assert p["num_q_tiles"] == -(-Nq // bm) and p["grid"] == 2 * 4 * p["num_q_tiles"]
     assert p["kv_tiles"] == 2 * 4 * _window_key_tiles(Nq, Nk, causal, window, bm, bn)
-    for D, dt in ((64, fa.FA_F16), (128, fa.FA_FP8_E4M3)):
-        q = fa.plan(2, Nq, Nk, 4, 2, D, causal=causal, window=window, dtype=dt)
+    q = fa.plan(2, Nq, Nk, 4, 2, 64, causal=causal, window=window, dtype=fa.FA_F16)
+    assert (q["block_m"], q["block_n"], q["waves"]) == (128, 32 if few else 64, 4)
+    assert q["kv_tiles"] == 2 * 4 * _window_key_tiles(Nq, Nk, causal, window, 128, q["block_n"])
+    for D in (64, 128):
+        q = fa.plan(2, Nq, Nk, 4, 2, D, causal=causal, window=window, dtype=fa.FA_FP8_E4M3)
         assert (q["block_m"], q["block_n"], q["waves"]) == (128, 64, 4)
     with pytest.raises(fa.FaError):
         fa.plan(1, 128, 128, 3, 2, 64)
