@@ -142,7 +142,7 @@ struct TileShape {
 // Whether a fp16/bf16 call takes the few-keys launch shape (4-wave workgroups, 32-key tiles):
 // every row admits at most kShortRowKeys keys (a window) and the call is dense or packed, not
 // block-sparse.
-constexpr int kShortRowKeys = 1024;
+constexpr int kShortRowKeys = 4096;
 bool short_rows(int D, int dtype, int causal, int wl, int wr, bool sparse);
 TileShape tile_shape(int D, int dtype, bool few_keys);
 hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, int block_n, int64_t grid, hipStream_t stream);

@@ -216,10 +216,11 @@ def _window_key_tiles(Nq, Nk, causal, window, block_m, block_n):
 
 
 @pytest.mark.parametrize("causal,window,few", [(False, (100, 30), True), (True, (256, 256), True),
-                                               (True, (1023, -1), True), (True, (1024, -1), False),
-                                               (False, (1000, 100), False), (False, (100, -1), False)])
+                                               (True, (4095, -1), True), (True, (4096, -1), False),
+                                               (False, (1000, 100), True), (False, (4000, 100), False),
+                                               (False, (100, -1), False)])
 def test_plan_few_keys_launch_shape(lib, causal, window, few):
-    # fp16/bf16 calls whose rows admit at most 1024 keys take 4-wave workgroups with 32-key tiles;
+    # fp16/bf16 calls whose rows admit at most 4096 keys take 4-wave workgroups with 32-key tiles;
     # other calls keep 64-key tiles (8 waves at D = 128, 4 at D = 64). fp8 never changes.
     Nq, Nk = 1000, 1100
     p = fa.plan(2, Nq, Nk, 4, 2, 128, causal=causal, window=window, dtype=fa.FA_BF16)

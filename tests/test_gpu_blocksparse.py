@@ -53,7 +53,7 @@ def test_blocksparse_all_ones_is_dense_bitwise(dtype):
     q, k, v = draw_qkv(B, N, N, Hq, Hkv, D, seed=9)
     q, k, v, _ = to_storage(q, k, v, dtype)
     ones = torch.ones(1, -(-N // 128), -(-N // 64), dtype=torch.uint8)
-    # A dense call whose rows admit at most 1024 keys takes the few-keys launch shape (32-key
+    # A dense call whose rows admit at most 4096 keys takes the few-keys launch shape (32-key
     # tiles, sums in another order); the window with an open right side keeps the dense call on
     # the 64-key kernel the block-sparse variant is built from.
     for causal, window in ((True, (-1, -1)), (False, (100, -1))):
