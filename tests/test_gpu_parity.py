@@ -52,6 +52,11 @@ RAGGED = [
     (3, 190, 190, 6, 3, 128, True, (64, -1)),
     (1, 640, 640, 2, 1, 64, False, (100, 100)),
     (1, 384, 384, 2, 2, 64, False, (-1, -1)),
+    # windows of at most 4096 keys a row run the few-keys launch shape (32-key tiles): key
+    # counts that are not a multiple of 32, Nq != Nk, rows with no admitted key
+    (2, 150, 333, 4, 2, 64, False, (50, 20)),
+    (1, 1000, 700, 2, 1, 128, True, (200, -1)),
+    (1, 97, 4100, 2, 2, 128, False, (4000, 95)),
 ]
 
 
