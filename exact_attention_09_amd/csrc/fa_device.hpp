@@ -107,9 +107,16 @@ __device__ inline float pair_sum(float x) {
 // these loads itself (vmcnt before each barrier). There is no destination register: nothing in the
 // register file is left pending. M0 (which addresses the LDS side) is saved and restored inside
 // the block, so the compiler's view of it never changes; the s_nop is the wait state between a
-// write of M0 and its use by the load. The LDS address and the offset are wave-uniform; they pass
-// through readfirstlane because the compiler sometimes keeps a uniform loop value in a vector
-// register, and the instruction takes scalar operands only.
+// write of M0 and its use by the load. The LDS address is wave-uniform; it passes through
+// readfirstlane because the compiler sometimes keeps a uniform loop value in a vector register,
+// and the instruction takes scalar operands only.
+//
+// Bounds. On this family the buffer range check compares only the per-lane (VGPR) offset with
+// the descriptor's byte count; an offset given in the instruction's scalar field is added after
+// the check. A tile's byte offset (`soff`, wave-uniform) therefore moves the descriptor itself:
+// its base advances by soff and its byte count shrinks by soff (to 0 past the end), so a lane
+// whose row lies past the tensor's span reads zeros instead of the memory that follows it. The
+// arithmetic is scalar (SALU): soff passes through readfirstlane.
 struct BufDesc {
   uint32_t w[4];
 };
@@ -117,33 +124,48 @@ __device__ inline BufDesc make_desc(const void* base, uint32_t bytes) {
   const uint64_t a = (uint64_t)(uintptr_t)base;
   return BufDesc{{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, bytes, kRsrcWord3}};
 }
-__device__ inline void dma16(const BufDesc& d, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
+// The descriptor of the same tensor seen from byte offset off (wave-uniform): base + off and
+// max(bytes - off, 0) addressable bytes.
+__device__ inline BufDesc desc_at(const BufDesc& d, uint32_t off) {
+  off = __builtin_amdgcn_readfirstlane(off);
+  const uint64_t a = (((uint64_t)(d.w[1] & 0xFFFFu) << 32) | d.w[0]) + off;
+  // max(bytes, off) - off on the scalar unit (written as a select, the compiler picks a clamped
+  // vector subtract and a readfirstlane)
+  uint32_t hi;
+  asm("s_max_u32 %0, %1, %2" : "=s"(hi) : "s"(d.w[2]), "s"(off));
+  const uint32_t n = hi - off;
+  auto u = [](uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane(x); };
+  return BufDesc{{u((uint32_t)a), u((d.w[1] & 0xFFFF0000u) | ((uint32_t)(a >> 32) & 0xFFFFu)), u(n), d.w[3]}};
+}
+__device__ inline void dma16(const BufDesc& d0, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const BufDesc d = desc_at(d0, soff);
   const u32x4 rs = u32x4{d.w[0], d.w[1], d.w[2], d.w[3]};
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dwordx4 %1, %2, %4 offen lds\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(voff), "s"(rs), "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "s"(__builtin_amdgcn_readfirstlane(soff))
+      : "v"(voff), "s"(rs), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
       : "memory");
 }
 // The 4-byte form: lane l's 4 bytes land at LDS byte address lds_addr + 4 * l.
-__device__ inline void dma4(const BufDesc& d, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
+__device__ inline void dma4(const BufDesc& d0, uint32_t voff, uint32_t soff, uint32_t lds_addr) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const BufDesc d = desc_at(d0, soff);
   const u32x4 rs = u32x4{d.w[0], d.w[1], d.w[2], d.w[3]};
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "buffer_load_dword %1, %2, %4 offen lds\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(voff), "s"(rs), "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "s"(__builtin_amdgcn_readfirstlane(soff))
+      : "v"(voff), "s"(rs), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
       : "memory");
 }
 // LDS reads addressed by 32-bit LDS byte addresses. Going through an integer address (instead of a

@@ -132,3 +132,30 @@ def test_bwd_benchmark_shape_tail(wl):
     T = 64
     ref = attention_bwd_fp64(decode(q[:, -T:]), decode(k), decode(v), decode(do[:, -T:]), scale, True, (-1, -1))
     check((got[0][:, -T:], got[1][:, -T:], got[2][:, -T:]), (ref[0], ref[1][:, -T:], ref[2][:, -T:]), q.dtype, wl)
+
+
+NAN_TAIL = [
+    # B, Nq, Nk, Hq, Hkv, D, causal, window: query and key counts off the tile grids
+    (1, 200, 333, 4, 2, 64, False, (-1, -1)),
+    (2, 150, 290, 4, 1, 128, True, (-1, -1)),
+    (1, 333, 200, 2, 2, 64, True, (-1, -1)),
+    (1, 100, 100, 8, 1, 64, True, (-1, -1)),      # MQA: the query heads are split over workgroups
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16], ids=["f16", "bf16"])
+@pytest.mark.parametrize("case", NAN_TAIL, ids=lambda c: "x".join(str(x) for x in c[:6]) + f"-c{int(c[6])}")
+def test_bwd_rows_past_the_end_are_not_read(case, dtype):
+    """q, k, v, out and dout are the first N rows of larger tensors whose remaining rows are NaN:
+    the last query and key tiles reach past N and must read zeros there (buffer range check)."""
+    from tests.gpu_util import nan_tailed
+    B, Nq, Nk, Hq, Hkv, D, causal, window = case
+    q, k, v, do = draw(B, Nq, Nk, Hq, Hkv, D, dtype, seed=Nq + 5 * Nk)
+    scale = D ** -0.5
+    qd, kd, vd, dod = nan_tailed(q), nan_tailed(k), nan_tailed(v), nan_tailed(do)
+    out, lse = fa.fwd(qd, kd, vd, causal=causal, window=window, softmax_scale=scale)
+    outd = nan_tailed(out)
+    dq, dk, dv = fa.bwd(qd, kd, vd, outd, dod, lse, causal=causal, window=window, softmax_scale=scale)
+    torch.cuda.synchronize()
+    ref = attention_bwd_fp64(decode(q), decode(k), decode(v), decode(do), scale, causal, window)
+    check((dq.cpu(), dk.cpu(), dv.cpu()), ref, dtype, f"nan tail {case}")
