@@ -64,3 +64,40 @@ def compare(dtype_name, out, lse, ref_o, ref_l, what=""):
     assert lse_err <= LSE_TOL, f"{what}: max |lse err| {lse_err} > {LSE_TOL}"
     stats["lse_err"] = lse_err
     return stats
+
+
+def oracle_heads(q, k, v, heads, rows, scale, causal, window, descale=None, workers=None):
+    """oracle_rows for each (b, h) of ``heads`` (same ``rows`` for every head), run on a pool of
+    host threads with single-threaded BLAS (numpy releases the GIL in its products and ufuncs).
+    Returns a list of (out [len(rows), D], lse [len(rows)]) in the order of ``heads``."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    n = workers or max(1, min(16, os.cpu_count() or 1))
+    with threadpool_limits(limits=1, user_api="blas"), ThreadPoolExecutor(max_workers=n) as ex:
+        futs = [ex.submit(oracle_rows, q, k, v, b, h, rows, scale, causal, window, descale) for b, h in heads]
+        return [f.result() for f in futs]
+
+
+def nan_outputs(B, Nq, Hq, D, out_dtype, device="cuda"):
+    """out [B, Nq, Hq, D] and lse [B, Hq, Nq] filled with NaN, so that an element the kernel never
+    writes fails the comparison."""
+    out = torch.full((B, Nq, Hq, D), float("nan"), dtype=out_dtype, device=device)
+    lse = torch.full((B, Hq, Nq), float("nan"), dtype=torch.float32, device=device)
+    return out, lse
+
+
+def nan_tailed(x, extra=128, device="cuda"):
+    """x [B, N, H, D] on the device as the first N rows of a [B, N + extra, H, D] tensor whose other
+    rows are NaN (e4m3: code 0x7F). A kernel that reads rows past N of a head reads NaN inside the
+    same allocation, which shows in its output without leaving the allocation."""
+    B, N, H, D = x.shape
+    if x.dtype == torch.float8_e4m3fn:
+        big = torch.full((B, N + extra, H, D), 0x7F, dtype=torch.uint8, device=device)
+        big[:, :N] = x.view(torch.uint8).to(device)
+        return big.view(torch.float8_e4m3fn)[:, :N]
+    big = torch.full((B, N + extra, H, D), float("nan"), dtype=x.dtype, device=device)
+    big[:, :N] = x.to(device)
+    return big[:, :N]
