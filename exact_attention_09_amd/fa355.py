@@ -108,6 +108,32 @@ def _strides(q, k, v, o) -> FaStrides:
     return s
 
 
+def _expect(t, name, shape, dtype, device, contiguous=False):
+    """Raise unless tensor t has the given shape, dtype and device (and is contiguous if asked)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected dtype {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _check_fwd(q, k, v, out, lse, code):
+    """Shapes, dtypes and devices of a dense forward call: q [B, Nq, Hq, D]; k, v [B, Nk, Hkv, D] of
+    q's dtype; out [B, Nq, Hq, D] of the output dtype; lse a contiguous fp32 [B, Hq, Nq] or None."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError(f"q and k must be [batch, seqlen, heads, headdim], got {tuple(q.shape)}, {tuple(k.shape)}")
+    B, Nq, Hq, D = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    _expect(k, "k", (B, Nk, Hkv, D), q.dtype, q.device)
+    _expect(v, "v", (B, Nk, Hkv, D), q.dtype, q.device)
+    _expect(out, "out", (B, Nq, Hq, D), _OUT_DTYPE[code], q.device)
+    if lse is not None:
+        _expect(lse, "lse", (B, Hq, Nq), torch.float32, q.device, contiguous=True)
+
+
 def fwd_raw(q, k, v, out, lse, causal=False, window=(-1, -1), softmax_scale=None, descale=None,
             stream=None) -> int:
     """Call fa_fwd on caller-provided tensors; returns the status code (0 = ok) without raising."""
@@ -115,6 +141,7 @@ def fwd_raw(q, k, v, out, lse, causal=False, window=(-1, -1), softmax_scale=None
     code = _DTYPE_CODE.get(q.dtype)
     if code is None:
         raise TypeError(f"unsupported dtype {q.dtype}")
+    _check_fwd(q, k, v, out, lse, code)
     B, Nq, Hq, D = q.shape
     Nk, Hkv = k.shape[1], k.shape[2]
     scale = float(D) ** -0.5 if softmax_scale is None else float(softmax_scale)
@@ -164,8 +191,11 @@ def fwd_blocksparse_raw(q, k, v, out, lse, block_mask, causal=False, window=(-1,
     code = _DTYPE_CODE.get(q.dtype)
     if code is None:
         raise TypeError(f"unsupported dtype {q.dtype}")
+    _check_fwd(q, k, v, out, lse, code)
     B, Nq, Hq, D = q.shape
     Nk, Hkv = k.shape[1], k.shape[2]
+    if block_mask.device != q.device:
+        raise ValueError("block_mask must be on q's device")
     if block_mask.dtype != torch.uint8 or block_mask.dim() != 3 or not block_mask.is_contiguous():
         raise ValueError("block_mask must be a contiguous uint8 [mask_heads, nqb, nkb] tensor")
     nqb, nkb = -(-Nq // 128), -(-Nk // 64)
@@ -202,8 +232,18 @@ def fwd_varlen_raw(q, k, v, out, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, 
     code = _DTYPE_CODE.get(q.dtype)
     if code is None:
         raise TypeError(f"unsupported dtype {q.dtype}")
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError(f"q and k must be [tokens, heads, headdim], got {tuple(q.shape)}, {tuple(k.shape)}")
     total_q, Hq, D = q.shape
     total_k, Hkv = k.shape[0], k.shape[1]
+    _expect(k, "k", (total_k, Hkv, D), q.dtype, q.device)
+    _expect(v, "v", (total_k, Hkv, D), q.dtype, q.device)
+    _expect(out, "out", (total_q, Hq, D), _OUT_DTYPE[code], q.device)
+    if lse is not None:
+        _expect(lse, "lse", (Hq, total_q), torch.float32, q.device, contiguous=True)
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.device != q.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor on q's device")
     B = cu_seqlens_q.numel() - 1
     if cu_seqlens_k.numel() != B + 1 or cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
         raise ValueError("cu_seqlens_q / cu_seqlens_k must be int32 tensors of B + 1 offsets")
@@ -265,8 +305,27 @@ def fwd_kvcache_raw(q, k_cache, v_cache, out, lse, seqlens_k, block_table, max_s
     code = _DTYPE_CODE.get(q.dtype)
     if code is None or code == FA_FP8_E4M3:
         raise TypeError(f"unsupported dtype {q.dtype}")
+    if q.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError(f"q and k_cache must be 4-d, got {tuple(q.shape)}, {tuple(k_cache.shape)}")
     B, Nq, Hq, D = q.shape
     Hkv = k_cache.shape[2]
+    if k_cache.shape[3] != D:
+        raise ValueError(f"k_cache head dimension {k_cache.shape[3]} != {D}")
+    if block_table is None and (k_cache.shape[0] != B or k_cache.shape[1] < max_seqlen_k):
+        raise ValueError(f"dense cache must be [{B}, >= max_seqlen_k = {max_seqlen_k}, Hkv, {D}], got "
+                         f"{tuple(k_cache.shape)}")
+    _expect(v_cache, "v_cache", tuple(k_cache.shape), q.dtype, q.device)
+    _expect(k_cache, "k_cache", tuple(k_cache.shape), q.dtype, q.device)
+    _expect(out, "out", (B, Nq, Hq, D), q.dtype, q.device)
+    if lse is not None:
+        _expect(lse, "lse", (B, Hq, Nq), torch.float32, q.device, contiguous=True)
+    _expect(seqlens_k, "seqlens_k", (B,), torch.int32, q.device, contiguous=True)
+    if block_table is not None:
+        if block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError(f"block_table must be [{B}, max_pages], got {tuple(block_table.shape)}")
+        _expect(block_table, "block_table", tuple(block_table.shape), torch.int32, q.device, contiguous=True)
+    if workspace is not None and workspace.device != q.device:
+        raise ValueError("workspace must be on q's device")
     scale = float(D) ** -0.5 if softmax_scale is None else float(softmax_scale)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -334,8 +393,17 @@ def bwd_raw(q, k, v, out, dout, lse, dq, dk, dv, workspace, causal=False, window
     code = _DTYPE_CODE.get(q.dtype)
     if code is None:
         raise TypeError(f"unsupported dtype {q.dtype}")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError(f"q and k must be [batch, seqlen, heads, headdim], got {tuple(q.shape)}, {tuple(k.shape)}")
     B, Nq, Hq, D = q.shape
     Nk, Hkv = k.shape[1], k.shape[2]
+    for name, t, shape in (("k", k, (B, Nk, Hkv, D)), ("v", v, (B, Nk, Hkv, D)), ("out", out, (B, Nq, Hq, D)),
+                           ("dout", dout, (B, Nq, Hq, D)), ("dq", dq, (B, Nq, Hq, D)), ("dk", dk, (B, Nk, Hkv, D)),
+                           ("dv", dv, (B, Nk, Hkv, D))):
+        _expect(t, name, shape, q.dtype, q.device)
+    _expect(lse, "lse", (B, Hq, Nq), torch.float32, q.device, contiguous=True)
+    if workspace.device != q.device:
+        raise ValueError("workspace must be on q's device")
     scale = float(D) ** -0.5 if softmax_scale is None else float(softmax_scale)
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream

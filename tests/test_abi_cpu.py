@@ -237,3 +237,45 @@ def test_plan_few_keys_launch_shape(lib, causal, window, few):
         assert (q["block_m"], q["block_n"], q["waves"]) == (128, 64, 4)
     with pytest.raises(fa.FaError):
         fa.plan(1, 128, 128, 3, 2, 64)
+
+
+# --- the binding rejects tensors the kernels would index out of bounds -----------------------
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(*shape, dtype=dtype or torch.float16)
+
+
+@pytest.mark.parametrize("what", ["v_shape", "k_dtype", "out_shape", "out_dtype", "lse_shape", "lse_dtype",
+                                  "lse_strided", "k_rank"])
+def test_binding_rejects_mismatched_tensors(lib, what):
+    import torch
+    q, k, v = _t(1, 64, 4, 64), _t(1, 80, 2, 64), _t(1, 80, 2, 64)
+    out, lse = _t(1, 64, 4, 64), torch.zeros(1, 4, 64)
+    if what == "v_shape":
+        v = _t(1, 79, 2, 64)
+    elif what == "k_dtype":
+        k = _t(1, 80, 2, 64, dtype=torch.bfloat16)
+    elif what == "out_shape":
+        out = _t(1, 64, 4, 32)
+    elif what == "out_dtype":
+        out = _t(1, 64, 4, 64, dtype=torch.bfloat16)
+    elif what == "lse_shape":
+        lse = torch.zeros(1, 64, 4)
+    elif what == "lse_dtype":
+        lse = torch.zeros(1, 4, 64, dtype=torch.float64)
+    elif what == "lse_strided":
+        lse = torch.zeros(1, 64, 4).transpose(1, 2)
+    elif what == "k_rank":
+        k = _t(80, 2, 64)
+    with pytest.raises((ValueError, TypeError)):
+        fa.fwd_raw(q, k, v, out, lse, stream=0)
+
+
+def test_binding_rejects_mismatched_bwd_tensors(lib):
+    import torch
+    q, k, v = _t(1, 64, 4, 64), _t(1, 80, 2, 64), _t(1, 80, 2, 64)
+    out, do, lse = _t(1, 64, 4, 64), _t(1, 64, 4, 64), torch.zeros(1, 4, 64)
+    dq, dk, dv = _t(1, 64, 4, 64), _t(1, 80, 2, 64), _t(1, 79, 2, 64)   # dv one row short
+    ws = torch.zeros(1 << 12)
+    with pytest.raises(ValueError):
+        fa.bwd_raw(q, k, v, out, do, lse, dq, dk, dv, ws, stream=0)
