@@ -154,6 +154,93 @@ def blas_threads():
         return 1, "unknown"
 
 
+def host_cpu_info():
+    """(model name, physical cores, logical CPUs this process may run on) of the host, from
+    /proc/cpuinfo (physical cores = distinct (physical id, core id) pairs)."""
+    model, cores = "unknown", set()
+    phys = core = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                key, _, val = line.partition(":")
+                key, val = key.strip(), val.strip()
+                if key == "model name" and model == "unknown":
+                    model = val
+                elif key == "physical id":
+                    phys = val
+                elif key == "core id":
+                    core = val
+                elif not key and phys is not None and core is not None:
+                    cores.add((phys, core))
+                    phys = core = None
+        if phys is not None and core is not None:
+            cores.add((phys, core))
+    except OSError:
+        pass
+    try:
+        logical = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        logical = os.cpu_count()
+    return model, (len(cores) or None), logical
+
+
+def host_note():
+    model, phys, logical = host_cpu_info()
+    return f"host CPU {model}, {phys} physical cores, {logical} logical CPUs available"
+
+
+class ClockSampler:
+    """Samples the GPU engine (gfx) clock while the step repeats (amd-smi's Python bindings from the
+    ROCm install; None where they cannot reach the device). The timed steps follow this window
+    directly and run on the same clock regime."""
+
+    _inited = None      # the amdsmi module once initialised, False if that failed
+
+    def __init__(self, device_index=0):
+        self.samples, self.source, self._h, self._smi = [], None, None, None
+        try:
+            if ClockSampler._inited is None:
+                ClockSampler._inited = False
+                sys.path.append("/opt/rocm/share/amd_smi")
+                import amdsmi
+                amdsmi.amdsmi_init()
+                ClockSampler._inited = amdsmi
+            amdsmi = ClockSampler._inited
+            if amdsmi is False:
+                return
+            handles = amdsmi.amdsmi_get_processor_handles()
+            h = handles[0] if len(handles) == 1 else None
+            if h is None:
+                import torch
+                bus = getattr(torch.cuda.get_device_properties(device_index), "pci_bus_id", None)
+                for c in handles:
+                    bdf = amdsmi.amdsmi_get_gpu_device_bdf(c)
+                    if bus is not None and int(bdf.split(":")[1], 16) == int(bus):
+                        h = c
+            if h is not None:
+                self._smi, self._h, self.source = amdsmi, h, "amd-smi gfx clock"
+        except Exception:
+            self._smi = None
+
+    def sample(self):
+        if self._smi is None:
+            return
+        try:
+            info = self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.GFX)
+            mhz = info.get("clk")
+            if isinstance(mhz, (int, float)) and mhz > 0:
+                self.samples.append(float(mhz))
+        except Exception:
+            self._smi = None
+
+    def summary(self):
+        if not self.samples:
+            return {"source": self.source or "unavailable", "samples": 0}
+        xs = sorted(self.samples)
+        return {"source": self.source, "samples": len(xs), "median_MHz": xs[len(xs) // 2],
+                "mean_MHz": round(sum(xs) / len(xs), 1), "min_MHz": xs[0], "max_MHz": xs[-1]}
+
+
 def cpu_baseline(w, q, k, v, descale, budget_s, dout=None):
     """Time the fp64 oracle on whole heads of the same inputs until budget_s has passed (the
     gradient oracle when dout is given)."""
@@ -194,14 +281,17 @@ def cpu_baseline(w, q, k, v, descale, budget_s, dout=None):
         if elapsed >= budget_s:
             break
     per_head_flops = metric_flops(w) * (1.0 if dout is None else BWD_FLOP_FACTOR) / (w.B * w.Hq)
+    model, phys, logical = host_cpu_info()
     return {
         "value": heads * per_head_flops / elapsed / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
+        "host": {"cpu_model": model, "physical_cores": phys, "logical_cpus": logical, "blas": blas_name,
+                 "blas_threads": int(threads)},
         "sample": f"{heads} of {w.B * w.Hq} (batch, head) pairs of the same inputs{' (gradients)' if dout is not None else ''}, full fp64 score matrix per "
                   f"head, {elapsed:.1f} s wall; metric FLOPs of those heads / wall time; BLAS={blas_name} "
-                  f"threads={threads}, host logical CPUs={os.cpu_count()}",
+                  f"threads={threads}, {host_note()}",
     }
 
 
@@ -215,6 +305,8 @@ def main():
                     help="time the forward pass (default, the headline metric) or the backward pass")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                     help="oracle time budget on the host; 0 skips the CPU baseline")
+    ap.add_argument("--no-bars", dest="bars", action="store_false",
+                    help="with the default workload, skip the other bar configurations (bf16, fp8, long GQA)")
     ap.add_argument("--cold-launches", type=int, default=10,
                     help="launches timed after writing 512 MiB (cold L2/MALL); 0 skips them")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -267,6 +359,42 @@ def main():
             sys.exit(2)
         return bench_varlen(args, VARLEN_WORKLOADS[args.workload], dev)
     w = WORKLOADS[args.workload]
+    bwd = args.pass_ == "bwd"
+    if bwd and w.dtype == "e4m3":
+        print(json.dumps({"error": "the backward pass takes fp16 or bf16 inputs"}))
+        sys.exit(2)
+    clock = ClockSampler()
+    rec = bench_dense(args, w, dev, bwd, clock=clock, cold_launches=args.cold_launches,
+                      cpu_seconds=args.cpu_baseline_seconds)
+    rec["clock"] = clock.summary()
+    if not bwd and args.workload == DEFAULT_WORKLOAD and args.bars:
+        # the other configurations the throughput bars are stated on, measured in the same run
+        rec["bars"] = {}
+        for name in BAR_WORKLOADS:
+            bc = ClockSampler()
+            r = bench_dense(args, WORKLOADS[name], dev, False, clock=bc, cold_launches=0, cpu_seconds=0)
+            rf = r["roofline"]
+            rec["bars"][name] = {
+                "dtype": r["dtype"], "ms_per_step": r["ms_per_step"], "TFLOPs": r["value"],
+                "pct_of_mfma_peak": r["pct_of_mfma_peak"], "kernel_avg_us": rf["kernel_avg_us"],
+                "roofline": {key: rf[key] for key in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
+                "clock": bc.summary()}
+    print(json.dumps(rec), flush=True)
+
+
+# Configurations of the throughput bars measured beside the default workload: the same shape in
+# bf16, the fp8 workload, and the long GQA workload (causal, and with the (256, 256) window).
+BAR_WORKLOADS = ["causal_b4_h32_n4096_d64_bf16", "causal_fp8_b2_h32_n4096_d64_e4m3",
+                 "gqa_b1_hq32_hkv8_n16384_d128_bf16", "gqa_win256_b1_hq32_hkv8_n16384_d128_bf16"]
+
+
+def bench_dense(args, w, dev, bwd, clock=None, cold_launches=0, cpu_seconds=0.0):
+    """One fa_fwd (or fa_bwd) workload in the timing protocol; returns its JSON record."""
+    import torch
+
+    import exact_attention_09_amd as fa
+    from exact_attention_09_amd.inputs import make_inputs
+
     seed = w.seeds[0]
     q, k, v, descale = make_inputs(w, seed)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
@@ -274,10 +402,6 @@ def main():
                       device=dev)
     lse = torch.empty(w.B, w.Hq, w.Nq, dtype=torch.float32, device=dev)
     scale = w.softmax_scale()
-    bwd = args.pass_ == "bwd"
-    if bwd and w.dtype == "e4m3":
-        print(json.dumps({"error": "the backward pass takes fp16 or bf16 inputs"}))
-        sys.exit(2)
 
     def fwd_step():
         st = fa.fwd_raw(qd, kd, vd, out, lse, w.causal, w.window, scale, descale)
@@ -300,14 +424,14 @@ def main():
                 raise fa.FaError(st, fa.status_str(st))
 
     stream = torch.cuda.current_stream(dev)     # fa_fwd launches on this stream
-    ms_per_step, avg_kernel_s, med_kernel_s, tinfo = timed(step, args, stream)
+    ms_per_step, avg_kernel_s, med_kernel_s, tinfo = timed(step, args, stream, clock)
 
     # Cold-cache variant: 512 MiB written between launches evicts L2 and the MALL.
     cold = None
-    if args.cold_launches > 0:
+    if cold_launches > 0:
         flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         cold_ms = []
-        for i in range(args.cold_launches):
+        for i in range(cold_launches):
             flush.fill_(i & 0xFF)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -317,7 +441,7 @@ def main():
             cold_ms.append(e0.elapsed_time(e1))
         del flush
         cold_med = sorted(cold_ms)[len(cold_ms) // 2] / 1e3
-        cold = {"launches": args.cold_launches, "kernel_median_us": round(cold_med * 1e6, 3),
+        cold = {"launches": cold_launches, "kernel_median_us": round(cold_med * 1e6, 3),
                 "TFLOPs": round(metric_flops(w) * (BWD_FLOP_FACTOR if bwd else 1.0) / cold_med / 1e12, 2)}
 
     flops = metric_flops(w) * (BWD_FLOP_FACTOR if bwd else 1.0)
@@ -361,16 +485,16 @@ def main():
         rec["cold_cache"] = cold
     if bwd:
         rec["config"]["pass"] = "bwd"
-    if args.cpu_baseline_seconds > 0:
-        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, descale, args.cpu_baseline_seconds,
-                                           dout if bwd else None)
-    print(json.dumps(rec), flush=True)
+    if cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v, descale, cpu_seconds, dout if bwd else None)
+    return rec
+
 
 
 PREHEAT_S = 0.25   # seconds of the step run before the timed region (engine clock ramp)
 
 
-def timed(step, args, stream):
+def timed(step, args, stream, clock=None):
     """The timing protocol of every bench line. W warm-up steps; K steps as a run that starts on an
     idle GPU sees them (reported as `unheated_ms_per_step`, not the value); the step repeated for
     PREHEAT_S seconds, because the engine clock rises over the first few tenths of a second under
@@ -398,10 +522,17 @@ def timed(step, args, stream):
     pre = 0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    # launches per burst: about 10 ms of queued work, so that the clock is sampled while the GPU
+    # is busy (half way through each burst) rather than across the gaps between bursts
+    burst = max(4, int(0.010 / max(unheated_s / max(args.steps, 1), 1e-6)))
     while time.perf_counter() - t0 < PREHEAT_S:
-        for _ in range(4):
+        tb = time.perf_counter()
+        for _ in range(burst):
             step()
-        pre += 4
+        pre += burst
+        if clock is not None:
+            time.sleep(max(0.0, 0.005 - (time.perf_counter() - tb)))
+            clock.sample()
         torch.cuda.synchronize()
     wall, events_s = back_to_back(args.steps)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -572,7 +703,7 @@ def cpu_baseline_sparse(w, q, k, v, mask, budget_s):
     return {"value": done_flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"the last {R} rows of {heads} of {w.Hq} heads (all their keys), fp64, {elapsed:.1f} s wall; "
                       f"admitted-pair FLOPs of those rows / wall time; BLAS={blas_name} threads={threads}, "
-                      f"host logical CPUs={os.cpu_count()}"}
+                      f"{host_note()}"}
 
 
 def kvcache_flops(w, lengths):
@@ -665,7 +796,7 @@ def cpu_baseline_kvcache(w, lengths, q, k, v, table, budget_s, alg_bytes):
     return {"value": done_bytes / elapsed / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{n_seq} of {len(lengths)} sequences of the same inputs (all heads), fp64, {elapsed:.1f} s wall; "
                       f"their share of the algorithmic bytes / wall time; BLAS={blas_name} threads={threads}, "
-                      f"host logical CPUs={os.cpu_count()}"}
+                      f"{host_note()}"}
 
 
 def cpu_baseline_varlen(w, lengths, q, k, v, cu_q, descale, budget_s):
@@ -702,7 +833,7 @@ def cpu_baseline_varlen(w, lengths, q, k, v, cu_q, descale, budget_s):
     return {"value": done_flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{n_pairs} of {len(lengths) * w.Hq} (sequence, head) pairs of the same inputs, full fp64 "
                       f"score matrix per pair, {elapsed:.1f} s wall; metric FLOPs of those pairs / wall time; "
-                      f"BLAS={blas_name} threads={threads}, host logical CPUs={os.cpu_count()}"}
+                      f"BLAS={blas_name} threads={threads}, {host_note()}"}
 
 
 if __name__ == "__main__":
