@@ -13,7 +13,7 @@
 #include "fa_mask.hpp"
 
 namespace fa {
-hipError_t launch_fwd_f16(const FwdArgs& a, int D, int dtype, int block_n, int64_t grid, hipStream_t stream);
+hipError_t launch_fwd_f16(const FwdArgs& a, int D, int dtype, int block_n, int qb, int64_t grid, hipStream_t stream);
 hipError_t launch_fwd_fp8(const FwdArgs& a, int D, int64_t grid, hipStream_t stream);
 
 bool short_rows(int D, int dtype, int causal, int wl, int wr, bool sparse) {
@@ -22,26 +22,30 @@ bool short_rows(int D, int dtype, int causal, int wl, int wr, bool sparse) {
   return right >= 0 && (int64_t)wl + right + 1 <= kShortRowKeys;
 }
 
-TileShape tile_shape(int D, int dtype, bool few_keys) {
+TileShape tile_shape(int D, int dtype, bool few_keys, bool sparse) {
   TileShape t;
   // fp16/bf16 at D = 128: 8 waves (two per SIMD, the register budget allows no more) and 64-key
-  // tiles, one workgroup per compute unit; otherwise 4 waves and 64-key tiles, two workgroups per
-  // compute unit. Rows that admit few keys (a window) make short workgroups whose pipeline start
-  // and end dominate; there, fp16/bf16 calls take 4 waves with 32-key tiles (half the LDS and
-  // fewer registers), so that more workgroups share a compute unit and overlap (two at D = 128,
-  // three at D = 64).
-  const bool wide = dtype != FA_FP8_E4M3 && D == 128 && !few_keys;
+  // tiles, one workgroup per compute unit. fp16/bf16 at D = 64: 4 waves of two 32-row query
+  // blocks each (256 rows) against 32-key tiles: every K and V operand read from LDS serves both
+  // blocks, which halves the LDS reads and the HBM -> LDS bytes per product. fp8 and block-sparse
+  // calls: 4 waves of one block against 64-key tiles. Rows that admit few keys (a window) make
+  // short workgroups whose pipeline start and end dominate; there, fp16/bf16 calls take 4 waves
+  // of one block with 32-key tiles (half the LDS and fewer registers), so that more workgroups
+  // share a compute unit and overlap (two at D = 128, three at D = 64).
+  const bool f16 = dtype != FA_FP8_E4M3;
+  const bool wide = f16 && D == 128 && !few_keys;
   t.waves = wide ? 8 : 4;
-  t.block_m = 32 * t.waves;
-  t.block_n = (few_keys && dtype != FA_FP8_E4M3) ? 32 : 64;
+  t.qb = (f16 && D == 64 && !few_keys && !sparse) ? 2 : 1;
+  t.block_m = 32 * t.waves * t.qb;
+  t.block_n = (f16 && (few_keys || t.qb == 2)) ? 32 : 64;
   const int es = dtype == FA_FP8_E4M3 ? 1 : 2;
   t.lds_bytes = (3 + 3) * t.block_n * D * es;   // three-slot K and V rings
   return t;
 }
 
-hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, int block_n, int64_t grid, hipStream_t stream) {
+hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, const TileShape& ts, int64_t grid, hipStream_t stream) {
   if (dtype == FA_FP8_E4M3) return launch_fwd_fp8(a, D, grid, stream);
-  return launch_fwd_f16(a, D, dtype, block_n, grid, stream);
+  return launch_fwd_f16(a, D, dtype, ts.block_n, ts.qb, grid, stream);
 }
 }  // namespace fa
 
@@ -198,7 +202,7 @@ fa_status fa_fwd_plan(int B, int Nq, int Nk, int Hq, int Hkv, int D, int causal,
   const fa_status st = check_sizes(B, Nq, Nk, Hq, Hkv, D, window_left, window_right, dtype);
   if (st != FA_OK) return st;
   const fa::TileShape ts =
-      fa::tile_shape(D, dtype, fa::short_rows(D, dtype, causal, window_left, window_right, false));
+      fa::tile_shape(D, dtype, fa::short_rows(D, dtype, causal, window_left, window_right, false), false);
   info->block_m = ts.block_m;
   info->block_n = ts.block_n;
   info->waves = ts.waves;
@@ -281,11 +285,12 @@ fa_status fwd_impl(const void* q, const void* k, const void* v, void* out, float
   a.mask_heads = mask_heads;
   a.nqb = (Nq + fa::kSparseBlockQ - 1) / fa::kSparseBlockQ;
   a.nkb = (Nk + fa::kSparseBlockK - 1) / fa::kSparseBlockK;
+  const bool sparse = block_mask != nullptr;
   const fa::TileShape ts =
-      fa::tile_shape(D, dtype, fa::short_rows(D, dtype, causal, window_left, window_right, block_mask != nullptr));
+      fa::tile_shape(D, dtype, fa::short_rows(D, dtype, causal, window_left, window_right, sparse), sparse);
   a.num_q_tiles = (Nq + ts.block_m - 1) / ts.block_m;
   const int64_t grid = (int64_t)B * Hq * a.num_q_tiles;
-  const hipError_t e = fa::launch_fwd(a, D, dtype, ts.block_n, grid, stream);
+  const hipError_t e = fa::launch_fwd(a, D, dtype, ts, grid, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -375,10 +380,11 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, 
   a.mask_heads = a.nqb = a.nkb = 0;
   a.total_q = total_q;
   a.total_k = total_k;
-  const fa::TileShape ts = fa::tile_shape(D, dtype, fa::short_rows(D, dtype, causal, window_left, window_right, false));
+  const fa::TileShape ts =
+      fa::tile_shape(D, dtype, fa::short_rows(D, dtype, causal, window_left, window_right, false), false);
   a.num_q_tiles = (max_seqlen_q + ts.block_m - 1) / ts.block_m;
   const int64_t grid = (int64_t)B * Hq * a.num_q_tiles;
-  const hipError_t e = fa::launch_fwd(a, D, dtype, ts.block_n, grid, stream);
+  const hipError_t e = fa::launch_fwd(a, D, dtype, ts, grid, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

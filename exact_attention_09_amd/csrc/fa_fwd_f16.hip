@@ -8,10 +8,12 @@
 // causal / window / MQA-GQA options of its Workflow 2.
 //
 // Mapping onto CDNA4:
-//  * One workgroup per (batch, query head, tile of BM = 32 * WAVES query rows); each 64-lane
-//    wave owns 32 query rows. The grid is remapped so that the workgroups one XCD receives
-//    (hardware deals blocks round-robin over the 8 XCDs) cover whole heads: a head's K/V stays
-//    in that XCD's L2. Under a causal mask a head's heaviest query tiles start first.
+//  * One workgroup per (batch, query head, tile of BM = 32 * QB * WAVES query rows); each 64-lane
+//    wave owns QB consecutive blocks of 32 query rows. With QB = 2 (head dimension 64) every K
+//    and V operand a wave reads from LDS serves both of its blocks, which halves the LDS reads
+//    and the HBM -> LDS bytes per product. The grid is remapped so that the workgroups one XCD
+//    receives (hardware deals blocks round-robin over the 8 XCDs) cover whole heads: a head's K/V
+//    stays in that XCD's L2. Under a causal mask a head's heaviest query tiles start first.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_{f16,bf16}: K rows
 //    are the A operand (read from LDS), Q rows the B operand (kept in registers). In the 32x32
 //    accumulator, lane l holds query l % 32 and 16 of the 32 keys; lanes l and l ^ 32 share a
@@ -42,10 +44,11 @@
 
 namespace fa {
 
-template <class TR, int D, int BN, int WAVES, bool SP>
+template <class TR, int D, int BN, int WAVES, int QB, bool SP>
 __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   constexpr int NT = WAVES * 64;        // threads per workgroup
-  constexpr int BM = WAVES * 32;        // query rows per workgroup
+  constexpr int WR = 32 * QB;           // query rows per wave: QB blocks of 32
+  constexpr int BM = WAVES * WR;        // query rows per workgroup
   constexpr int ES = 2;                 // bytes per stored element
   constexpr int ROWB = D * ES;          // bytes per K/V row in LDS
   constexpr int TILEB = BN * ROWB;      // bytes per K (or V) tile
@@ -56,9 +59,10 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   constexpr int KS = D / 16;            // MFMA k-steps over the head dimension
   static_assert(BN * CPR % NT == 0, "tile must split evenly over the workgroup");
   static_assert(ROWB == 128 || ROWB == 256, "swizzles are laid out for 128- or 256-byte rows");
+  static_assert(!SP || QB == 1, "block-sparse launches keep one query block per wave");
 
   constexpr int NS = 3;                 // ring slots per tensor
-  __shared__ __attribute__((aligned(16))) char smem[2 * NS * TILEB];  // [K0 K1 K2 | V0 V1 V2]
+  __shared__ __attribute__((aligned(16))) char smem[2 * NS * TILEB];  // [K slots | V slots]
   char* const kring = smem;
   char* const vring = smem + NS * TILEB;
 
@@ -66,7 +70,7 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5;      // half of the wave: which 16 of a block's 32 keys / k-slots
-  const int l32 = lane & 31;     // query column of this lane inside the wave's 32 rows
+  const int l32 = lane & 31;     // query column of this lane inside each 32-row block of the wave
 
   // ---- which (batch, head, query tile) this workgroup computes
   int b, h, qt;
@@ -87,13 +91,13 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   const uint32_t q_rowb = (uint32_t)(a.q_n * ES), k_rowb = (uint32_t)(a.k_n * ES);
   const uint32_t v_rowb = (uint32_t)(a.v_n * ES), o_rowb = (uint32_t)(a.o_n * ES);
 
-  // ---- K/V tiles this workgroup visits, and this wave's rows
+  // ---- K/V tiles this workgroup visits, and this wave's rows (QB consecutive blocks of 32)
   const int wg_last = min(q0 + BM, sv.Nq) - 1;
   int tb, te;
   tile_range(ms, q0, wg_last, BN, &tb, &te);
-  const int w0 = q0 + wave * 32;
+  const int w0 = q0 + wave * WR;
   const bool wave_live = w0 < sv.Nq;
-  const int w1 = min(w0 + 31, sv.Nq - 1);
+  const int w1 = min(w0 + WR - 1, sv.Nq - 1);
   // Key bounds of the wave's first and last rows, clamped to [-1, Nk] (wave-uniform scalars).
   // Each row admits an interval of keys and both ends grow with the row, so the tiles holding
   // an admitted key for some row of the wave form an interval [jlo, jhi), and the tiles admitted
@@ -109,10 +113,16 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
     jhi = min(te, whi1 / BN + 1);
   }
   const int flo = (wlo1 + BN - 1) / BN, fhi = (whi0 + 1) / BN;
-  const int my_row = w0 + l32;
-  const int lo_i = clamp_key(key_lo(ms, my_row));
-  const int hi_i = clamp_key(key_hi(ms, my_row));
-  const uint32_t span_i = hi_i >= lo_i ? (uint32_t)(hi_i - lo_i + 1) : 0u;
+  // this lane's query row in each block, and the keys it admits: [lo_i, lo_i + span_i)
+  int my_row[QB], lo_i[QB];
+  uint32_t span_i[QB];
+#pragma unroll
+  for (int qb2 = 0; qb2 < QB; ++qb2) {
+    my_row[qb2] = w0 + qb2 * 32 + l32;
+    lo_i[qb2] = clamp_key(key_lo(ms, my_row[qb2]));
+    const int hi_i = clamp_key(key_hi(ms, my_row[qb2]));
+    span_i[qb2] = hi_i >= lo_i[qb2] ? (uint32_t)(hi_i - lo_i[qb2] + 1) : 0u;
+  }
 
   // ---- block-sparse: the tiles of [tb, te) that the block mask sets for one of the workgroup's
   // mask rows, compacted into LDS by wave 0 (sp_list: tile ids, then a bit per mask row, then the
@@ -123,7 +133,7 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   if constexpr (SP) {
     const int mr0 = q0 / kSparseBlockQ;
     const int nrows = min(BM / kSparseBlockQ, a.nqb - mr0);
-    sp_row = (q0 + wave * 32) / kSparseBlockQ - mr0;
+    sp_row = (q0 + wave * WR) / kSparseBlockQ - mr0;
     const uint8_t* mrow = a.block_mask + ((int64_t)(a.mask_heads == 1 ? 0 : h) * a.nqb + mr0) * a.nkb;
     if (wave == 0) {
       int cnt = 0;
@@ -157,9 +167,9 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   };
   const int pb0 = SP ? 0 : tb, pe = SP ? sp_n : te;   // step positions pb0 .. pe
 
-  // Q operands (B operand of S^T): row my_row, head-dim slots ks*16 + hl*8 .. +7; loaded in the
-  // prologue, behind the first K/V tile loads
-  i32x4 qop[KS];
+  // Q operands (B operand of S^T): block qb2's row, head-dim slots ks*16 + hl*8 .. +7; loaded in
+  // the prologue, behind the first K/V tile loads
+  i32x4 qop[QB][KS];
 
   // ---- HBM -> LDS loads of one K or V tile. Load i of a thread writes the 16 bytes at slot
   // position P = (i * NT + tid) * 16; P holds row P / ROWB, physical chunk (P % ROWB) / 16, i.e.
@@ -204,28 +214,38 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   }
 
   const float c2 = a.scale_log2;
-  // Reference max of score * c2 for this lane's query. It starts at a huge negative finite value
-  // rather than -inf: the first tile with an admitted key then overflows the sum bound and sets
-  // the reference (see kSumBound), while a fully masked tile still gives p = exp2(-inf) = 0.
-  float m = -1e30f;
-  float l = 0.f;         // this lane's share of the running sum (lanes l, l^32 split the keys)
-  f32x16 o[DB];
+  // Reference max of score * c2 for this lane's query in each block. It starts at a huge negative
+  // finite value rather than -inf: the first tile with an admitted key then overflows the sum
+  // bound and sets the reference (see kSumBound), while a fully masked tile still gives
+  // p = exp2(-inf) = 0.
+  float m[QB], l[QB];    // l: this lane's share of the running sum (lanes l, l^32 split the keys)
+  f32x16 o[QB][DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = f32x16{};
+  for (int qb2 = 0; qb2 < QB; ++qb2) {
+    m[qb2] = -1e30f;
+    l[qb2] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[qb2][db] = f32x16{};
+  }
 
   // ---- building blocks of one step
-  // S MFMA number e of a tile (k-step e / KB, key block e % KB): consecutive MFMAs alternate
-  // accumulators, so dependent ones are KB apart.
-  auto mfma_s = [&](const i32x4& kop, f32x16 (&s)[KB], int e) { s[e % KB] = TR::mfma(kop, qop[e / KB], s[e % KB]); };
-  // PV MFMA number e of a tile (key block e / (2 DB), half (e / DB) % 2, column block e % DB).
-  auto mfma_pv = [&](const i32x4& vop, const uint32_t (&pk)[KB][8], int e) {
-    const int kb = e / (2 * DB), half = (e / DB) % 2, db = e % DB;
-    const i32x4 pop = i32x4{(int)pk[kb][4 * half + 0], (int)pk[kb][4 * half + 1], (int)pk[kb][4 * half + 2],
-                            (int)pk[kb][4 * half + 3]};
-    o[db] = TR::mfma(vop, pop, o[db]);
+  // Products of a tile, numbered in issue order. S MFMA i: K operand i / QB (k-step (i/QB) / KB,
+  // key block (i/QB) % KB) against query block i % QB, so each K operand read from LDS serves the
+  // QB blocks back to back; accumulators that depend on each other are KB * QB products apart.
+  // PV MFMA i: V operand i / QB (key block, half, column block), query block i % QB.
+  auto mfma_s = [&](const i32x4& kop, f32x16 (&s)[QB][KB], int i) {
+    const int u = i / QB, qb2 = i % QB;
+    s[qb2][u % KB] = TR::mfma(kop, qop[qb2][u / KB], s[qb2][u % KB]);
   };
-  // Softmax of score pair number i (key block i / 8, accumulator entries 2 (i % 8) and + 1):
-  // p = exp2(s * c - mref), packed to the MFMA type, added to the row sum.
+  auto mfma_pv = [&](const i32x4& vop, const uint32_t (&pk)[QB][KB][8], int i) {
+    const int u = i / QB, qb2 = i % QB;
+    const int kb = u / (2 * DB), half = (u / DB) % 2, db = u % DB;
+    const i32x4 pop = i32x4{(int)pk[qb2][kb][4 * half + 0], (int)pk[qb2][kb][4 * half + 1],
+                            (int)pk[qb2][kb][4 * half + 2], (int)pk[qb2][kb][4 * half + 3]};
+    o[qb2][db] = TR::mfma(vop, pop, o[qb2][db]);
+  };
+  // Softmax of score pair number i of query block qb2 (key block i / 8, accumulator entries
+  // 2 (i % 8) and + 1): p = exp2(s * c - mref), packed to the MFMA type, added to the row sum.
   auto p_pair = [&](const f32x16 (&sc)[KB], uint32_t (&pk)[KB][8], float& rs, float mref, int i) {
     const int kb = i / 8, r = (i % 8) * 2;
     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][r], c2, -mref));
@@ -233,44 +253,50 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
     pk[kb][r >> 1] = TR::pack(p0, p1);
     rs = TR::sum2(rs, pk[kb][r >> 1], p0, p1);
   };
-  constexpr int NSM = KS * KB;          // S MFMAs per tile
-  constexpr int NPV = KB * 2 * DB;      // PV MFMAs per tile
-  constexpr int NPAIR = KB * 8;         // score pairs per lane per tile
+  constexpr int NK = KS * KB;           // K operands per tile
+  constexpr int NV = KB * 2 * DB;       // V operands per tile
+  constexpr int NSM = NK * QB;          // S MFMAs per tile
+  constexpr int NPV = NV * QB;          // PV MFMAs per tile
+  constexpr int NPB = KB * 8;           // score pairs per lane per tile and query block
+  constexpr int NPAIR = NPB * QB;
   static_assert(NSM == NPV && (2 * NSM) % NPAIR == 0, "the interleave pairs S and PV MFMAs one to one");
   auto softmax_all = [&](f32x16 (&sc)[KB], uint32_t (&pk)[KB][8], float& rs, float mref) {
     rs = 0.f;
 #pragma unroll
-    for (int i = 0; i < NPAIR; ++i) p_pair(sc, pk, rs, mref, i);
+    for (int i = 0; i < NPB; ++i) p_pair(sc, pk, rs, mref, i);
   };
   // Rebase when a p may exceed the bound (see kSumBound): m moves to the running max, O and l
   // are rescaled, p is recomputed. O must already hold every PV product issued against the old m.
-  auto check_rebase = [&](f32x16 (&sc)[KB], uint32_t (&pk)[KB][8], float& rs) {
+  auto check_rebase = [&](f32x16 (&sc)[KB], uint32_t (&pk)[KB][8], float& rs, int qb2) {
     if (__builtin_amdgcn_ballot_w64(!(rs <= kSumBound))) {
       float mx = sc[0][0];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-      const float m_new = fmaxf(m, pair_max(mx) * c2);   // finite: m starts finite
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      l *= alpha;
+      const float m_new = fmaxf(m[qb2], pair_max(mx) * c2);   // finite: m starts finite
+      const float alpha = __builtin_amdgcn_exp2f(m[qb2] - m_new);
+      l[qb2] *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-      m = m_new;
-      softmax_all(sc, pk, rs, m);
+      for (int db = 0; db < DB; ++db) o[qb2][db] *= alpha;
+      m[qb2] = m_new;
+      softmax_all(sc, pk, rs, m[qb2]);
     }
-    l += rs;
+    l[qb2] += rs;
   };
-  auto mask_tile = [&](f32x16 (&sc)[KB], int t) {
+  auto mask_tile = [&](f32x16 (&sc)[QB][KB], int t) {
     // key of accumulator r in block kb is t*BN + kb*32 + (r/4)*8 + hl*4 + r%4
-    const int jl = t * BN + hl * 4 - lo_i;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int qb2 = 0; qb2 < QB; ++qb2) {
+      const int jl = t * BN + hl * 4 - lo_i[qb2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = jl + kb * 32 + (r >> 2) * 8 + (r & 3);
-        sc[kb][r] = (uint32_t)j < span_i ? sc[kb][r] : -INFINITY;
-      }
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = jl + kb * 32 + (r >> 2) * 8 + (r & 3);
+          sc[qb2][kb][r] = (uint32_t)j < span_i[qb2] ? sc[qb2][kb][r] : -INFINITY;
+        }
+    }
   };
 
   // ---- software pipeline. Step j: loads of K(j+3) and V(j+1) are issued; then PV(j-1) and
@@ -288,10 +314,10 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   const int need_lo = jlo - 1;
   const uint32_t need_n = jlo < jhi ? (uint32_t)(jhi - jlo + 2) : 0u;
   const uint32_t full_n = fhi > flo ? (uint32_t)(fhi - flo) : 0u;
+
   uint32_t r0 = 0, r1 = TILEB, r2 = 2 * TILEB;
   uint32_t k_soff = (uint32_t)((tb + 3) * BN) * k_rowb;   // byte offset of K(j+3)
   uint32_t v_soff = (uint32_t)((tb + 1) * BN) * v_rowb;   // byte offset of V(j+1)
-
   // V slot 2 stands for V(tb-1), read (against P = 0) by the first step before any load fills
   // it: zero it so that the product is exactly zero.
 #pragma unroll
@@ -306,32 +332,40 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
     if (pb0 + 2 < pe) dma(k_d, kgoff, (uint32_t)(t2 * BN) * k_rowb, kring_a + 2 * TILEB);
   }
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-    qop[ks] = __builtin_amdgcn_raw_buffer_load_b128(q_r, (uint32_t)my_row * q_rowb + (ks * 16 + hl * 8) * ES, 0, 0);
+  for (int qb2 = 0; qb2 < QB; ++qb2)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qop[qb2][ks] = __builtin_amdgcn_raw_buffer_load_b128(q_r, (uint32_t)my_row[qb2] * q_rowb + (ks * 16 + hl * 8) * ES,
+                                                           0, 0);
   // Q (and with it the first tiles) must have landed before the pipelined loop: without this
   // wait the compiler's wait-count analysis, merging the loop back edge, would make every
   // iteration wait on the prefetches.
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   barrier_keep(0);
-  f32x16 sa[KB], sb[KB];
-  uint32_t pa[KB][8], pb[KB][8];
+  f32x16 sa[QB][KB], sb[QB][KB];
+  uint32_t pa[QB][KB][8], pb[QB][KB][8];
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
+  for (int qb2 = 0; qb2 < QB; ++qb2)
 #pragma unroll
-    for (int r = 0; r < 8; ++r) pa[kb][r] = pb[kb][r] = 0u;
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 8; ++r) pa[qb2][kb][r] = pb[qb2][kb][r] = 0u;
   {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) sa[kb] = f32x16{};
+    for (int qb2 = 0; qb2 < QB; ++qb2)
 #pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      const uint32_t base = opaque_vbase(kring_a + koff[k]);
+      for (int kb = 0; kb < KB; ++kb) sa[qb2][kb] = f32x16{};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) mfma_s(lds_read_b128(base + kb * 32 * ROWB), sa, k * KB + kb);
+    for (int u = 0; u < NK; ++u) {
+      const i32x4 kop = lds_read_b128(opaque_vbase(kring_a + koff[u / KB]) + (u % KB) * 32 * ROWB);
+#pragma unroll
+      for (int qb2 = 0; qb2 < QB; ++qb2) mfma_s(kop, sa, u * QB + qb2);
     }
   }
   barrier_keep(0);   // every wave has read K(tb) before step tb refills its slot
 
-  auto step = [&](int j, f32x16 (&sc)[KB], f32x16 (&sn)[KB], const uint32_t (&pp)[KB][8], uint32_t (&pc)[KB][8]) {
+  auto step = [&](int j, f32x16 (&sc)[QB][KB], f32x16 (&sn)[QB][KB], const uint32_t (&pp)[QB][KB][8],
+                  uint32_t (&pc)[QB][KB][8]) {
     const bool k3 = j + 3 < pe, v1 = j + 1 < pe;
     if (k3) dma(k_d, kgoff, SP ? (uint32_t)(sp_tile(j + 3) * BN) * k_rowb : k_soff, kring_a + r0);
     if (v1) dma(v_d, vgoff, SP ? (uint32_t)(sp_tile(j + 1) * BN) * v_rowb : v_soff, vring_a + r1);
@@ -340,62 +374,69 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
         const int tj = sp_tile(j);
         if (!sp_admits(j)) {
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb) sc[kb] = f32x16{} - INFINITY;
+          for (int kb = 0; kb < KB; ++kb) sc[0][kb] = f32x16{} - INFINITY;
         } else if (!((uint32_t)(tj - flo) < full_n)) {
           mask_tile(sc, tj);
         }
       } else {
         if (!((uint32_t)(j - flo) < full_n)) mask_tile(sc, j);
       }
-      // Operand of MFMA e of the sequence (even e: S, K from LDS; odd e: PV, V^T from LDS), read
-      // PF MFMAs ahead of its use. At D = 64 every read is issued up front (registers allow it
-      // and it measured fastest) and each MFMA waits only for its own operand (the compiler's
-      // per-use waits); at D = 128 a short distance keeps the kernel within 256
-      // registers, so two waves share each SIMD.
+      // Operand u of the step (even u: K operand u / 2, read by rows from LDS; odd u: V^T
+      // operand u / 2, read by transpose reads), read PF operands ahead of its first use. At
+      // D = 64 every read is issued up front (registers allow it and it measured fastest) and
+      // each MFMA waits only for its own operand (the compiler's per-use waits); at D = 128 a
+      // short distance keeps the kernel within 256 registers, so two waves share each SIMD.
       const uint32_t kslot = kring_a + r1, vslot = vring_a + r2;   // K(j+1), V(j-1)
       uint32_t kbase[KS], vbase[DB];
 #pragma unroll
       for (int k = 0; k < KS; ++k) kbase[k] = opaque_vbase(kslot + koff[k]);
 #pragma unroll
       for (int db = 0; db < DB; ++db) vbase[db] = opaque_vbase(vslot + voff[db]);
-      constexpr int NM = 2 * NSM, PF = D == 64 ? NM : 3;
-      i32x4 opnd[NM];
-      auto read_operand = [&](int e) {
-        const int idx = e / 2;
-        if (e % 2 == 0) {
-          opnd[e] = lds_read_b128(kbase[idx / KB] + (idx % KB) * 32 * ROWB);
+      constexpr int NOP = NK + NV, NM = NSM + NPV, PF = D == 64 ? NOP : 3;
+      i32x4 opnd[NOP];
+      auto read_operand = [&](int u) {
+        const int idx = u / 2;
+        if (u % 2 == 0) {
+          opnd[u] = lds_read_b128(kbase[idx / KB] + (idx % KB) * 32 * ROWB);
         } else {
           const int kb = idx / (2 * DB), half = (idx / DB) % 2, db = idx % DB;
           const uint32_t p = vbase[db] + (kb * 32 + half * 16) * ROWB;
           const i32x2 v0 = lds_read_tr16(p), v1 = lds_read_tr16(p + 8 * ROWB);
-          opnd[e] = i32x4{v0[0], v0[1], v1[0], v1[1]};
+          opnd[u] = i32x4{v0[0], v0[1], v1[0], v1[1]};
         }
       };
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) sn[kb] = f32x16{};
-      float rs = 0.f;
+      for (int qb2 = 0; qb2 < QB; ++qb2)
 #pragma unroll
-      for (int e = 0; e < PF; ++e) read_operand(e);
+        for (int kb = 0; kb < KB; ++kb) sn[qb2][kb] = f32x16{};
+      float rs[QB];
+#pragma unroll
+      for (int qb2 = 0; qb2 < QB; ++qb2) rs[qb2] = 0.f;
+#pragma unroll
+      for (int u = 0; u < PF; ++u) read_operand(u);
       // The sequence runs at raised issue priority: when both waves of a SIMD are ready, the one
       // inside its sequence (which feeds both pipes) issues first.
       __builtin_amdgcn_s_setprio(1);
       __builtin_amdgcn_sched_barrier(0);
-      constexpr int PER = 2 * NSM / NPAIR;   // MFMAs per score pair
+      constexpr int PER = NM / NPAIR;   // MFMAs per score pair
 #pragma unroll
       for (int e = 0; e < NM; ++e) {
-        if (e + PF < NM) read_operand(e + PF);
-        if (e % 2 == 0) mfma_s(opnd[e], sn, e / 2);
-        else mfma_pv(opnd[e], pp, e / 2);
+        // MFMA e: S MFMA e / 2 (even e) or PV MFMA e / 2 (odd e); operand u of the step
+        const int i = e / 2, u = 2 * (i / QB) + (e % 2);
+        if (i % QB == 0 && u + PF < NOP) read_operand(u + PF);
+        if (e % 2 == 0) mfma_s(opnd[u], sn, i);
+        else mfma_pv(opnd[u], pp, i);
         if (e % PER == PER - 1) {
-          const int pi = e / PER;
-          p_pair(sc, pc, rs, m, pi);
+          const int pi = e / PER, qb2 = pi / NPB, pj = pi % NPB;
+          p_pair(sc[qb2], pc[qb2], rs[qb2], m[qb2], pj);
           // keep the pair in this group (the compiler would otherwise gather the softmax)
-          asm volatile("" ::"v"(pc[pi / 8][pi % 8]), "v"(rs));
+          asm volatile("" ::"v"(pc[qb2][pj / 8][pj % 8]), "v"(rs[qb2]));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_s_setprio(0);
-      check_rebase(sc, pc, rs);
+#pragma unroll
+      for (int qb2 = 0; qb2 < QB; ++qb2) check_rebase(sc[qb2], pc[qb2], rs[qb2], qb2);
     }
     // K(j+2) and V(j) must have landed for the next step; this step's loads stay in flight
     barrier_keep(CH * ((int)k3 + (int)v1));
@@ -416,43 +457,54 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
     if (t + 2 > pe) break;
   }
 
+
   // ---- epilogue: O / l, lse = (m + log2 l) * ln 2
-  if (!wave_live || my_row >= sv.Nq) return;
-  const float l_tot = pair_sum(l);
-  const float inv = l_tot > 0.f ? a.out_scale / l_tot : 0.f;
+  if (!wave_live) return;
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int qb2 = 0; qb2 < QB; ++qb2) {
+    const float l_tot = pair_sum(l[qb2]);
+    if (my_row[qb2] >= sv.Nq) continue;
+    const float inv = l_tot > 0.f ? a.out_scale / l_tot : 0.f;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const uint32_t w0v = TR::pack(o[db][4 * q4 + 0] * inv, o[db][4 * q4 + 1] * inv);
-      const uint32_t w1v = TR::pack(o[db][4 * q4 + 2] * inv, o[db][4 * q4 + 3] * inv);
-      __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)w0v, (int)w1v}, o_r,
-                                            (uint32_t)my_row * o_rowb + (db * 32 + q4 * 8 + hl * 4) * ES, 0, 0);
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const uint32_t w0v = TR::pack(o[qb2][db][4 * q4 + 0] * inv, o[qb2][db][4 * q4 + 1] * inv);
+        const uint32_t w1v = TR::pack(o[qb2][db][4 * q4 + 2] * inv, o[qb2][db][4 * q4 + 3] * inv);
+        __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)w0v, (int)w1v}, o_r,
+                                              (uint32_t)my_row[qb2] * o_rowb + (db * 32 + q4 * 8 + hl * 4) * ES, 0, 0);
+      }
+    if (a.lse != nullptr && hl == 0) {
+      const float lse = l_tot > 0.f ? (m[qb2] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
+      a.lse[sv.lse0 + my_row[qb2]] = lse;
     }
-  if (a.lse != nullptr && hl == 0) {
-    const float lse = l_tot > 0.f ? (m + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
-    a.lse[sv.lse0 + my_row] = lse;
   }
 }
 
 template <class TR, int D>
-static hipError_t launch_t(const FwdArgs& a, int block_n, int64_t grid, hipStream_t stream) {
+static hipError_t launch_t(const FwdArgs& a, int block_n, int qb, int64_t grid, hipStream_t stream) {
   constexpr int BN = 64, WAVES = D == 64 ? 4 : 8;
   static_assert(BN == kSparseBlockK && (WAVES * 32) % kSparseBlockQ == 0, "tiles nest in the mask's blocks");
   if (a.block_mask != nullptr)
-    hipLaunchKernelGGL((fa_fwd_kernel<TR, D, BN, WAVES, true>), dim3((unsigned)grid), dim3(WAVES * 64),
+    hipLaunchKernelGGL((fa_fwd_kernel<TR, D, BN, WAVES, 1, true>), dim3((unsigned)grid), dim3(WAVES * 64),
                        (size_t)(2 * a.nkb + 1) * 4, stream, a);
-  else if (block_n == 32)   // rows with few keys: 4 waves, 32-key tiles
-    hipLaunchKernelGGL((fa_fwd_kernel<TR, D, 32, 4, false>), dim3((unsigned)grid), dim3(4 * 64), 0, stream, a);
+  else if (qb == 2) {   // D = 64: two query blocks per wave, 32-key tiles
+    if constexpr (D == 64)
+      hipLaunchKernelGGL((fa_fwd_kernel<TR, D, 32, 4, 2, false>), dim3((unsigned)grid), dim3(4 * 64), 0, stream, a);
+    else
+      return hipErrorInvalidValue;
+  } else if (block_n == 32)   // rows with few keys: 4 waves, 32-key tiles
+    hipLaunchKernelGGL((fa_fwd_kernel<TR, D, 32, 4, 1, false>), dim3((unsigned)grid), dim3(4 * 64), 0, stream, a);
   else
-    hipLaunchKernelGGL((fa_fwd_kernel<TR, D, BN, WAVES, false>), dim3((unsigned)grid), dim3(WAVES * 64), 0, stream, a);
+    hipLaunchKernelGGL((fa_fwd_kernel<TR, D, BN, WAVES, 1, false>), dim3((unsigned)grid), dim3(WAVES * 64), 0, stream,
+                       a);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_f16(const FwdArgs& a, int D, int dtype, int block_n, int64_t grid, hipStream_t stream) {
+hipError_t launch_fwd_f16(const FwdArgs& a, int D, int dtype, int block_n, int qb, int64_t grid, hipStream_t stream) {
   if (dtype == 0)
-    return D == 64 ? launch_t<F16, 64>(a, block_n, grid, stream) : launch_t<F16, 128>(a, block_n, grid, stream);
-  return D == 64 ? launch_t<BF16, 64>(a, block_n, grid, stream) : launch_t<BF16, 128>(a, block_n, grid, stream);
+    return D == 64 ? launch_t<F16, 64>(a, block_n, qb, grid, stream) : launch_t<F16, 128>(a, block_n, qb, grid, stream);
+  return D == 64 ? launch_t<BF16, 64>(a, block_n, qb, grid, stream) : launch_t<BF16, 128>(a, block_n, qb, grid, stream);
 }
 
 }  // namespace fa

@@ -180,12 +180,13 @@ def test_causal_4096_tile_counts():
 
 
 def test_plan(lib):
-    # 4 waves of 32 query rows per workgroup: 32 query tiles of 128 rows, and query tile qt visits
-    # 2 (qt + 1) key tiles of 64 under a causal mask
+    # D = 64, fp16/bf16: 4 waves of two 32-row query blocks per workgroup: 16 query tiles of 256
+    # rows, and query tile qt visits 8 (qt + 1) key tiles of 32 under a causal mask
     p = fa.plan(4, 4096, 4096, 32, 32, 64, causal=True)
-    assert p["block_m"] == 128 and p["block_n"] == 64 and p["waves"] == 4 and p["num_q_tiles"] == 32
-    assert p["grid"] == 4 * 32 * 32
-    assert p["kv_tiles"] == 4 * 32 * sum(2 * (t + 1) for t in range(32))
+    assert p["block_m"] == 256 and p["block_n"] == 32 and p["waves"] == 4 and p["num_q_tiles"] == 16
+    assert p["grid"] == 4 * 32 * 16
+    assert p["kv_tiles"] == 4 * 32 * sum(8 * (t + 1) for t in range(16))
+    assert p["lds_bytes"] == 6 * 32 * 64 * 2
     # D = 128 runs 8 waves (256 rows per workgroup)
     p = fa.plan(1, 16384, 16384, 32, 8, 128, causal=True, dtype=fa.FA_BF16)
     assert p["block_m"] == 256 and p["waves"] == 8 and p["num_q_tiles"] == 64
@@ -221,7 +222,7 @@ def _window_key_tiles(Nq, Nk, causal, window, block_m, block_n):
                                                (False, (100, -1), False)])
 def test_plan_few_keys_launch_shape(lib, causal, window, few):
     # fp16/bf16 calls whose rows admit at most 4096 keys take 4-wave workgroups with 32-key tiles;
-    # other calls keep 64-key tiles (8 waves at D = 128, 4 at D = 64). fp8 never changes.
+    # other calls at D = 128 keep 8 waves and 64-key tiles. fp8 never changes.
     Nq, Nk = 1000, 1100
     p = fa.plan(2, Nq, Nk, 4, 2, 128, causal=causal, window=window, dtype=fa.FA_BF16)
     bm, bn = (128, 32) if few else (256, 64)
@@ -229,9 +230,10 @@ def test_plan_few_keys_launch_shape(lib, causal, window, few):
     assert p["lds_bytes"] == 6 * bn * 128 * 2
     assert p["num_q_tiles"] == -(-Nq // bm) and p["grid"] == 2 * 4 * p["num_q_tiles"]
     assert p["kv_tiles"] == 2 * 4 * _window_key_tiles(Nq, Nk, causal, window, bm, bn)
+    # D = 64: the few-keys shape, else 4 waves of two 32-row blocks (256 rows) against 32-key tiles
     q = fa.plan(2, Nq, Nk, 4, 2, 64, causal=causal, window=window, dtype=fa.FA_F16)
-    assert (q["block_m"], q["block_n"], q["waves"]) == (128, 32 if few else 64, 4)
-    assert q["kv_tiles"] == 2 * 4 * _window_key_tiles(Nq, Nk, causal, window, 128, q["block_n"])
+    assert (q["block_m"], q["block_n"], q["waves"]) == (128 if few else 256, 32, 4)
+    assert q["kv_tiles"] == 2 * 4 * _window_key_tiles(Nq, Nk, causal, window, q["block_m"], q["block_n"])
     for D in (64, 128):
         q = fa.plan(2, Nq, Nk, 4, 2, D, causal=causal, window=window, dtype=fa.FA_FP8_E4M3)
         assert (q["block_m"], q["block_n"], q["waves"]) == (128, 64, 4)

@@ -1,7 +1,8 @@
 """GPU parity of fa_fwd_blocksparse (through the C ABI) against the fp64 block-sparse oracle
 (``oracle.blocksparse``, reading RS1). Bars as for the dense forward: fp16 max|dout| <= 2e-3,
 bf16 <= 1.5e-2, lse within 1e-3, rows with no admitted key exactly 0 / -inf. An all-ones mask must
-give bitwise the dense kernel's result (masked tiles add exact zeros)."""
+give bitwise the dense kernel's result where the dense call runs the same tile shape (D = 128;
+masked tiles add exact zeros), and the oracle's result where it does not (D = 64)."""
 import numpy as np
 import pytest
 import torch
@@ -9,7 +10,7 @@ import torch
 import exact_attention_09_amd as fa
 from exact_attention_09_amd.inputs import SPARSE_WORKLOADS, draw_qkv, sparse_block_mask, to_storage
 from oracle import admitted, attention_blocksparse_fp64, attention_rows_fp64, block_admitted
-from tests.gpu_util import compare, decode, out_to_f64
+from tests.gpu_util import compare, decode, oracle_full, out_to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -48,20 +49,29 @@ def test_blocksparse_matches_oracle(case, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
-def test_blocksparse_all_ones_is_dense_bitwise(dtype):
-    B, N, Hq, Hkv, D = 2, 700, 4, 2, 128 if dtype == "bf16" else 64
+@pytest.mark.parametrize("D", [64, 128])
+def test_blocksparse_all_ones_is_dense(dtype, D):
+    """An all-ones mask admits what the dense mask admits. At D = 128 the dense launch is the
+    64-key kernel the block-sparse variant is built from, so the results are bitwise equal; at
+    D = 64 the dense launch takes two 32-row query blocks per wave against 32-key tiles (its sums
+    run in another order), so both are held to the oracle instead."""
+    B, N, Hq, Hkv = 2, 700, 4, 2
     q, k, v = draw_qkv(B, N, N, Hq, Hkv, D, seed=9)
     q, k, v, _ = to_storage(q, k, v, dtype)
     ones = torch.ones(1, -(-N // 128), -(-N // 64), dtype=torch.uint8)
     # A dense call whose rows admit at most 4096 keys takes the few-keys launch shape (32-key
-    # tiles, sums in another order); the window with an open right side keeps the dense call on
-    # the 64-key kernel the block-sparse variant is built from.
+    # tiles); the window with an open right side keeps the dense call off it.
     for causal, window in ((True, (-1, -1)), (False, (100, -1))):
         so, sl = run(q, k, v, ones, causal, window, 0.1)
         do, dl = fa.fwd(q.cuda(), k.cuda(), v.cuda(), causal, window, 0.1)
         torch.cuda.synchronize()
-        assert torch.equal(so.view(torch.int16), do.cpu().view(torch.int16))
-        assert torch.equal(sl, dl.cpu())
+        if D == 128:
+            assert torch.equal(so.view(torch.int16), do.cpu().view(torch.int16))
+            assert torch.equal(sl, dl.cpu())
+        else:
+            ro, rl = oracle_full(q, k, v, 0.1, causal, window)
+            for o, l, what in ((so, sl, "sparse all-ones"), (do.cpu(), dl.cpu(), "dense")):
+                compare(dtype, out_to_f64(o), l.numpy().astype(np.float64), ro, rl, f"{what} D{D} c{causal}")
 
 
 @pytest.mark.parametrize("name", list(SPARSE_WORKLOADS))
