@@ -8,6 +8,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/fa355.h"
 #include "fa_kernels.hpp"
 #include "fa_mask.hpp"
@@ -169,7 +171,8 @@ const char* fa_status_str(fa_status s) {
     case FA_ERR_DESCALE: return "fp8 e4m3 needs descale_qkv";
     case FA_ERR_LAUNCH: return "kernel launch failed";
     case FA_ERR_TOO_LARGE: return "one head of a tensor spans 2^31 bytes or more";
-    case FA_ERR_WORKSPACE: return "fa_bwd workspace smaller than fa_bwd_workspace_bytes";
+    case FA_ERR_WORKSPACE: return "workspace smaller than the sizes need (fa_bwd_workspace_bytes, fa_fwd_kvcache_workspace_bytes)";
+    case FA_ERR_SCRATCH: return "the sizes need more split scratch than fa_fwd_kvcache_noalloc's fixed FA_NOALLOC_SCRATCH_BYTES";
   }
   return "unknown status";
 }
@@ -393,11 +396,25 @@ size_t fa_fwd_kvcache_workspace_bytes(int B, int Nq, int Hq, int Hkv, int D, int
   return (size_t)dec_workspace_floats(B, Nq, Hq, Hkv, D, max_seqlen_k) * 4u;
 }
 
-fa_status fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
-                         const int32_t* seqlens_k, const int32_t* block_table, int B, int Nq, int Hq, int Hkv, int D,
-                         int max_seqlen_k, int page_size, int max_pages_per_seq, int num_pages, const fa_strides* s,
-                         float softmax_scale, int causal, int window_left, int window_right, fa_dtype dtype,
-                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+}  // extern "C"
+
+// The fixed scratch of fa_fwd_kvcache_noalloc: one copy per GPU in the library's device code,
+// held until the process ends. Host code never uses the array's name as an address (on the host
+// it only stands for the symbol): the device address comes from hipGetSymbolAddress, resolved
+// once per device with that device current, and kept per device (scratch_ptr below).
+static __device__ __align__(256) char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// fa_fwd_kvcache, and fa_fwd_kvcache_noalloc when scratch_call is set: then `workspace` is not
+// known yet; it is resolved (scratch_ptr) after every argument check, and a need above
+// FA_NOALLOC_SCRATCH_BYTES is FA_ERR_SCRATCH.
+void* scratch_ptr();
+fa_status kvcache_impl(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                       const int32_t* seqlens_k, const int32_t* block_table, int B, int Nq, int Hq, int Hkv, int D,
+                       int max_seqlen_k, int page_size, int max_pages_per_seq, int num_pages, const fa_strides* s,
+                       float softmax_scale, int causal, int window_left, int window_right, fa_dtype dtype,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream, bool scratch_call) {
   if (!q || !k_cache || !v_cache || !out || !seqlens_k || !s) return FA_ERR_NULL;
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
   fa_status st = check_kvcache_sizes(B, Nq, Hq, Hkv, D, max_seqlen_k);
@@ -406,7 +423,13 @@ fa_status fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache
   if (window_left < -1 || window_right < -1) return FA_ERR_WINDOW;
   if (!finite_pos(softmax_scale)) return FA_ERR_SCALE;
   const int64_t need = dec_workspace_floats(B, Nq, Hq, Hkv, D, max_seqlen_k) * 4;
-  if ((uint64_t)workspace_bytes < (uint64_t)need || (need > 0 && workspace == nullptr)) return FA_ERR_WORKSPACE;
+  if (scratch_call) {
+    if ((uint64_t)need > (uint64_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+    workspace_bytes = FA_NOALLOC_SCRATCH_BYTES;
+    workspace = nullptr;   // resolved below, once the other arguments are known to be valid
+  } else if ((uint64_t)workspace_bytes < (uint64_t)need || (need > 0 && workspace == nullptr)) {
+    return FA_ERR_WORKSPACE;
+  }
   const int64_t str[12] = {s->q_b, s->q_n, s->q_h, s->k_b, s->k_n, s->k_h, s->v_b, s->v_n, s->v_h, s->o_b, s->o_n, s->o_h};
   for (int i = 0; i < 12; ++i)
     if (str[i] < 0 || (str[i] * 2) % 16 != 0) return FA_ERR_STRIDES;
@@ -414,6 +437,10 @@ fa_status fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out) || !aligned16(workspace) ||
       ((uintptr_t)lse & 3u) || ((uintptr_t)seqlens_k & 3u) || ((uintptr_t)block_table & 3u))
     return FA_ERR_STRIDES;
+  if (scratch_call && need > 0) {
+    workspace = scratch_ptr();
+    if (workspace == nullptr) return FA_ERR_LAUNCH;
+  }
 
   fa::DecArgs a;
   a.q = q; a.kc = k_cache; a.vc = v_cache; a.o = out; a.lse = lse;
@@ -438,6 +465,48 @@ fa_status fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache
   a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
   const hipError_t e = fa::launch_decode(a, D, dtype, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The current device's scratch address (resolved on the first call on that device), or null if it
+// cannot be resolved.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                         const int32_t* seqlens_k, const int32_t* block_table, int B, int Nq, int Hq, int Hkv, int D,
+                         int max_seqlen_k, int page_size, int max_pages_per_seq, int num_pages, const fa_strides* s,
+                         float softmax_scale, int causal, int window_left, int window_right, fa_dtype dtype,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return kvcache_impl(q, k_cache, v_cache, out, lse, seqlens_k, block_table, B, Nq, Hq, Hkv, D, max_seqlen_k,
+                      page_size, max_pages_per_seq, num_pages, s, softmax_scale, causal, window_left, window_right,
+                      dtype, workspace, workspace_bytes, stream, false);
+}
+
+fa_status fa_fwd_kvcache_noalloc(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                                 const int32_t* seqlens_k, const int32_t* block_table, int B, int Nq, int Hq,
+                                 int Hkv, int D, int max_seqlen_k, int page_size, int max_pages_per_seq,
+                                 int num_pages, const fa_strides* s, float softmax_scale, int causal,
+                                 int window_left, int window_right, fa_dtype dtype, hipStream_t stream) {
+  return kvcache_impl(q, k_cache, v_cache, out, lse, seqlens_k, block_table, B, Nq, Hq, Hkv, D, max_seqlen_k,
+                      page_size, max_pages_per_seq, num_pages, s, softmax_scale, causal, window_left, window_right,
+                      dtype, nullptr, 0, stream, true);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int Nq, int Nk, int Hq, int Hkv, int D) {

@@ -20,7 +20,11 @@ _DTYPE_CODE = {torch.float16: FA_F16, torch.bfloat16: FA_BF16, torch.float8_e4m3
 _OUT_DTYPE = {FA_F16: torch.float16, FA_BF16: torch.bfloat16, FA_FP8_E4M3: torch.bfloat16}
 
 # Every symbol include/fa355.h declares.
-EXPORTED = ("fa_fwd", "fa_fwd_blocksparse", "fa_fwd_varlen", "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str", "fa_fwd_plan", "fa_kv_tile_range", "fa_version")
+EXPORTED = ("fa_fwd", "fa_fwd_blocksparse", "fa_fwd_varlen", "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_bytes",
+            "fa_fwd_kvcache_noalloc", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str", "fa_fwd_plan",
+            "fa_kv_tile_range", "fa_version")
+# FA_NOALLOC_SCRATCH_BYTES of include/fa355.h: the fixed per-device scratch of fa_fwd_kvcache_noalloc.
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class FaStrides(ctypes.Structure):
@@ -74,6 +78,9 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_kvcache.restype = c_int
     lib.fa_fwd_kvcache.argtypes = ([c_void_p] * 7 + [c_int] * 9 + [ctypes.POINTER(FaStrides), c_float, c_int, c_int,
                                    c_int, c_int, c_void_p, ctypes.c_size_t, c_void_p])
+    lib.fa_fwd_kvcache_noalloc.restype = c_int
+    lib.fa_fwd_kvcache_noalloc.argtypes = ([c_void_p] * 7 + [c_int] * 9 + [ctypes.POINTER(FaStrides), c_float, c_int,
+                                           c_int, c_int, c_int, c_void_p])
     lib.fa_fwd_kvcache_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_fwd_kvcache_workspace_bytes.argtypes = [c_int] * 6
     lib.fa_bwd.restype = c_int
@@ -297,10 +304,12 @@ def kvcache_workspace(q, Hkv, max_seqlen_k):
 
 
 def fwd_kvcache_raw(q, k_cache, v_cache, out, lse, seqlens_k, block_table, max_seqlen_k, num_pages=0,
-                    causal=False, window=(-1, -1), softmax_scale=None, workspace=None, stream=None) -> int:
+                    causal=False, window=(-1, -1), softmax_scale=None, workspace=None, stream=None,
+                    noalloc=False) -> int:
     """Call fa_fwd_kvcache on caller-provided tensors; returns the status code without raising.
     Dense cache: block_table None, k_cache/v_cache [B, max_seqlen_k, Hkv, D]. Paged: k_cache/v_cache
-    [num_pages, page_size, Hkv, D] and block_table int32 [B, max_pages_per_seq]."""
+    [num_pages, page_size, Hkv, D] and block_table int32 [B, max_pages_per_seq]. ``noalloc=True``
+    calls fa_fwd_kvcache_noalloc instead (no workspace: the library's fixed per-device scratch)."""
     lib = load()
     code = _DTYPE_CODE.get(q.dtype)
     if code is None or code == FA_FP8_E4M3:
@@ -333,6 +342,14 @@ def fwd_kvcache_raw(q, k_cache, v_cache, out, lse, seqlens_k, block_table, max_s
     max_pages = block_table.shape[1] if block_table is not None else 0
     npages = (num_pages or k_cache.shape[0]) if block_table is not None else 0
     st = _strides(q, k_cache, v_cache, out)
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("fa_fwd_kvcache_noalloc takes no workspace")
+        return lib.fa_fwd_kvcache_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
+                                          lse.data_ptr() if lse is not None else None, seqlens_k.data_ptr(),
+                                          block_table.data_ptr() if block_table is not None else None, B, Nq, Hq,
+                                          Hkv, D, int(max_seqlen_k), page_size, max_pages, npages, ctypes.byref(st),
+                                          scale, int(bool(causal)), int(window[0]), int(window[1]), code, stream)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     return lib.fa_fwd_kvcache(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
                               lse.data_ptr() if lse is not None else None, seqlens_k.data_ptr(),

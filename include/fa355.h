@@ -61,7 +61,8 @@ typedef enum fa_status {
   FA_ERR_DESCALE = 8,   /* FA_FP8_E4M3 without descale_qkv                                         */
   FA_ERR_LAUNCH = 9,    /* the kernel launch failed (HIP error; e.g. no device)                    */
   FA_ERR_TOO_LARGE = 10, /* one head's span of q, k, v or out reaches 2^31 bytes                   */
-  FA_ERR_WORKSPACE = 11  /* fa_bwd: workspace_bytes below fa_bwd_workspace_bytes of the sizes       */
+  FA_ERR_WORKSPACE = 11, /* fa_bwd / fa_fwd_kvcache: workspace_bytes below what the sizes need     */
+  FA_ERR_SCRATCH = 12    /* fa_fwd_kvcache_noalloc: the sizes need more than FA_NOALLOC_SCRATCH_BYTES */
 } fa_status;
 
 /* Element strides (not bytes) of the batch, seqlen and head axes; the headdim stride is 1. */
@@ -196,6 +197,30 @@ fa_status fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache
 /* Bytes of workspace fa_fwd_kvcache needs for these sizes (0 when the keys are not split, and for
  * invalid sizes). Pure host function. */
 size_t fa_fwd_kvcache_workspace_bytes(int B, int Nq, int Hq, int Hkv, int D, int max_seqlen_k);
+
+/* Bytes of the per-device scratch array behind fa_fwd_kvcache_noalloc (64 MiB). */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * fa_fwd_kvcache_noalloc — fa_fwd_kvcache for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Same operation,
+ * kernels, arguments (minus workspace and workspace_bytes), results (bitwise) and errors as
+ * fa_fwd_kvcache. The split partials go to a fixed scratch array of FA_NOALLOC_SCRATCH_BYTES bytes
+ * in the library's device code, one per GPU, which each GPU keeps until the process ends; the
+ * call allocates nothing (no hipMalloc, no hipFree, no allocating library routine).
+ *  - Runs on the current device; its first call on a device resolves the array's address there.
+ *  - FA_ERR_SCRATCH, before any device call, when fa_fwd_kvcache_workspace_bytes of the sizes
+ *    exceeds FA_NOALLOC_SCRATCH_BYTES; FA_ERR_LAUNCH if the array's address cannot be resolved.
+ *  - Calls on one GPU share its array: calls that overlap in time on one GPU (other streams or
+ *    threads without ordering between them) race and give undefined results. Calls ordered on a
+ *    stream are safe; the array keeps the last call's partials, and nothing needs clearing (each
+ *    call writes every partial it reads).
+ */
+fa_status fa_fwd_kvcache_noalloc(const void* q, const void* k_cache, const void* v_cache, void* out, float* lse,
+                                 const int32_t* seqlens_k, const int32_t* block_table, int B, int Nq, int Hq,
+                                 int Hkv, int D, int max_seqlen_k, int page_size, int max_pages_per_seq,
+                                 int num_pages, const fa_strides* strides, float softmax_scale, int causal,
+                                 int window_left, int window_right, fa_dtype dtype, hipStream_t stream);
 
 /* Element strides of the backward pass's tensors (headdim stride 1). */
 typedef struct fa_bwd_strides {

@@ -42,11 +42,11 @@ def test_exports_every_declared_symbol(lib):
 def test_version_and_status_strings(lib):
     assert lib.fa_version() >= 100
     seen = set()
-    for code in range(11):
+    for code in range(13):
         s = fa.status_str(code)
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 11
+    assert len(seen) == 13
     assert fa.status_str(99) == "unknown status"
 
 

@@ -90,3 +90,39 @@ def test_kvcache_rejects_bad_strides_and_alignment(lib):
         p[i] = P + 2
         assert call(lib, ptrs=p, page=16, max_pages=4, num_pages=8) == 6
     assert call(lib, ws=P + 8) == 6                       # the workspace: 16 bytes
+
+
+# --- fa_fwd_kvcache_noalloc: the same checks, and FA_ERR_SCRATCH before any device call --------
+def call_noalloc(lib, ptrs=None, B=2, Nq=1, Hq=8, Hkv=2, D=64, max_k=1024, page=0, max_pages=0, num_pages=0,
+                 st=None, scale=0.125, causal=0, wl=-1, wr=-1, dtype=1):
+    p = [P] * 6 + [None] if ptrs is None else ptrs
+    s = FaStrides(*(st or strides(B, Nq, Hq, Hkv, D, max_k)))
+    return lib.fa_fwd_kvcache_noalloc(*p, B, Nq, Hq, Hkv, D, max_k, page, max_pages, num_pages, ctypes.byref(s),
+                                      scale, causal, wl, wr, dtype, None)
+
+
+def test_noalloc_scratch_limit_matches_header(lib):
+    import re
+    text = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fa355.h")).read()
+    m = re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_rejects_what_fa_fwd_kvcache_rejects(lib):
+    for kw, code in [(dict(B=0), 2), (dict(D=80), 3), (dict(wl=-3), 4), (dict(scale=-1.0), 5), (dict(dtype=2), 7)]:
+        assert call_noalloc(lib, **kw) == code == call(lib, **kw)
+    p = [P] * 6 + [None]
+    p[0] = None
+    assert call_noalloc(lib, ptrs=p) == 1
+    p[0] = P + 8
+    assert call_noalloc(lib, ptrs=p) == 6
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    # 64 sequences x 64 query heads x 16 queries against 16 K/V heads and 2^20 keys: split
+    # partials of far more than the fixed scratch. Rejected before any device call.
+    B, Nq, Hq, Hkv, D, L = 64, 16, 64, 16, 128, 1 << 20
+    need = lib.fa_fwd_kvcache_workspace_bytes(B, Nq, Hq, Hkv, D, L)
+    assert need > fa.NOALLOC_SCRATCH_BYTES
+    assert call_noalloc(lib, B=B, Nq=Nq, Hq=Hq, Hkv=Hkv, D=D, max_k=L, st=strides(B, Nq, Hq, Hkv, D, L)) == 12
+    assert "FA_NOALLOC_SCRATCH_BYTES" in fa.status_str(12)
