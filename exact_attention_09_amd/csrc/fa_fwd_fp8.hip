@@ -13,8 +13,9 @@
 //    covers 64 keys of O^T = V^T P^T.
 //  * P is rounded to e4m3 after a 2^8 shift that keeps small weights above the format's
 //    subnormal range. To keep p * 2^8 <= 448 (the largest e4m3 value), the row reference m moves
-//    whenever a tile's row max exceeds it by more than 0.8 (log2 units): p <= 2^0.8. The running
-//    sum (and so the lse) uses the unrounded fp32 p.
+//    whenever a tile's row max exceeds it by more than 0.8 (log2 units): p <= 2^0.8; a move puts
+//    m 2 above the tile's max, so moves (and their rescaling of O) are rare. The running sum
+//    (and so the lse) uses the unrounded fp32 p.
 //  * V^T is read with ds_read_b64_tr_b8: a lane receives 8 consecutive LDS rows of one column.
 //    The 16 keys a lane half holds in the S^T accumulator (keys g*8 + half*4 + e, g, e < 4, of
 //    each 32-key block) are stored as 16 consecutive LDS rows (row half*16 + g*4 + e): the HBM ->
@@ -31,8 +32,14 @@ namespace fa {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // log2 of the 2^8 shift applied to p before its e4m3 rounding, and the reference threshold.
+// When the reference moves it is placed kLift above the tile's max, so that p <= 2^-kLift right
+// after the move and the next move needs a rise of kTau8 + kLift: fewer moves (each rescales O).
+// kLift is a whole number, so the weight of the max itself, 2^(8 - kLift) after the shift, is an
+// exact e4m3 value (as 2^8 was without the lift); weights down to 2^(-14 + kLift) of the row max
+// stay in e4m3's normal range.
 constexpr float kPShiftLog2 = 8.0f;
 constexpr float kTau8 = 0.8f;
+constexpr float kLift = 2.0f;
 
 // 64-bank LDS swizzles (16-byte chunk XOR) for 64- and 128-byte rows.
 template <int ROWB>
@@ -46,6 +53,14 @@ __device__ inline int v_swz8(int row) {
 // Key (within the tile) stored at LDS row rho of a V tile.
 __device__ inline int v_key_of_row(int rho) {
   return (rho & ~31) | (((rho >> 2) & 3) << 3) | (((rho >> 4) & 1) << 2) | (rho & 3);
+}
+
+// max(a, b, c) in one v_max3_f32. Written out because fmaxf makes the compiler canonicalise each
+// MFMA result first (an extra v_max per input); the scores here are finite or -inf, never NaN.
+__device__ inline float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 __device__ inline f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
@@ -259,25 +274,32 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_fp8_kernel(FwdArgs a) {
       for (int e = 0; e < NSM; ++e) kop[e] = k_operand(kring_a + r1, e);         // K(j+1)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) sn[kb] = f32x16{};
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
       const i32x8 pop = i32x8{pp[0], pp[1], pp[2], pp[3], pp[4], pp[5], pp[6], pp[7]};
-      // first half: PV(j-1) and the row max
+      // first half: PV(j-1) and the row max. Each PV MFMA follows a share of the max (which
+      // needs no LDS operand), so the V reads issued above have that long to land; each MFMA
+      // waits only for its own operand. Two max chains give the vector pipe independent work.
       __builtin_amdgcn_s_setprio(1);
       __builtin_amdgcn_sched_barrier(0);
-      float mx = sc[0][0];
+      float mx0 = sc[0][0], mx1 = sc[0][1];
       constexpr int MAXPER = KB * 16 / DB;   // max-ed values per PV MFMA
+      static_assert(MAXPER % 4 == 0, "two chains of three-input maxima");
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        o[db] = mfma_fp8(vop[db], pop, o[db]);
 #pragma unroll
-        for (int q = db * MAXPER; q < (db + 1) * MAXPER; ++q) mx = fmaxf(mx, sc[q / 16][q % 16]);
-        asm volatile("" ::"v"(mx));
+        for (int q = db * MAXPER; q < (db + 1) * MAXPER; q += 4) {
+          mx0 = max3(mx0, sc[q / 16][q % 16], sc[q / 16][q % 16 + 1]);
+          mx1 = max3(mx1, sc[q / 16][q % 16 + 2], sc[q / 16][q % 16 + 3]);
+        }
+        asm volatile("" ::"v"(mx0), "v"(mx1));
+        __builtin_amdgcn_sched_barrier(0);
+        o[db] = mfma_fp8(vop[db], pop, o[db]);
         __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_s_setprio(0);
-      // reference update (lazy: p <= 2^0.8 keeps 2^8 p inside the e4m3 range)
-      mx = pair_max(mx) * c2;
-      const float m_new = mx > m + kTau8 ? mx : m;
+      // reference update (lazy: p <= 2^0.8 keeps 2^8 p inside the e4m3 range). A move places the
+      // reference kLift above the tile's max, so the next move needs a rise of kTau8 + kLift.
+      const float mx = pair_max(fmaxf(mx0, mx1)) * c2;
+      const float m_new = mx > m + kTau8 ? mx + kLift : m;
       if (__builtin_amdgcn_ballot_w64(m_new != m)) {
         const float alpha = __builtin_amdgcn_exp2f(m - m_new);
         l *= alpha;
