@@ -130,8 +130,9 @@ def kernel_source_hash(pass_="fwd"):
     return h.hexdigest()[:16]
 
 
-def committed_traffic(workload, pass_="fwd"):
-    """HBM bytes per launch from the committed counter summary, if taken on this kernel source."""
+def committed_counters(workload, pass_="fwd"):
+    """The committed counter summary of the workload (profiles/traffic_<workload>.txt) if it was
+    taken on the current kernel source, else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -139,7 +140,24 @@ def committed_traffic(workload, pass_="fwd"):
         t = json.load(f)
     if t.get("kernel_source_hash") != kernel_source_hash(pass_):
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t
+
+
+def committed_traffic(workload, pass_="fwd"):
+    """HBM bytes per launch from the committed counter summary, if taken on this kernel source."""
+    t = committed_counters(workload, pass_)
+    return t.get("hbm_bytes_per_launch") if t else None
+
+
+def committed_clock(workload, pass_="fwd"):
+    """The engine clock under this workload's kernel, from the same committed counter run: GPU
+    busy cycles per XCD (GRBM_GUI_ACTIVE / 8) over the dispatch's duration. The SMU's own clock
+    reports are not live on every host, so the clock is taken from the counters."""
+    t = committed_counters(workload, pass_)
+    mhz = t.get("gfx_clock_MHz") if t else None
+    return {"MHz": mhz, "source": "GRBM_GUI_ACTIVE / 8 XCDs / dispatch duration, committed counter run of this "
+                                  f"kernel source (profiles/traffic_{workload}.txt)" if mhz else
+            "no counter run of this kernel source is committed"}
 
 
 def blas_threads():
@@ -187,58 +205,6 @@ def host_cpu_info():
 def host_note():
     model, phys, logical = host_cpu_info()
     return f"host CPU {model}, {phys} physical cores, {logical} logical CPUs available"
-
-
-class ClockSampler:
-    """Samples the GPU engine (gfx) clock while the step repeats (amd-smi's Python bindings from the
-    ROCm install; None where they cannot reach the device). The timed steps follow this window
-    directly and run on the same clock regime."""
-
-    _inited = None      # the amdsmi module once initialised, False if that failed
-
-    def __init__(self, device_index=0):
-        self.samples, self.source, self._h, self._smi = [], None, None, None
-        try:
-            if ClockSampler._inited is None:
-                ClockSampler._inited = False
-                sys.path.append("/opt/rocm/share/amd_smi")
-                import amdsmi
-                amdsmi.amdsmi_init()
-                ClockSampler._inited = amdsmi
-            amdsmi = ClockSampler._inited
-            if amdsmi is False:
-                return
-            handles = amdsmi.amdsmi_get_processor_handles()
-            h = handles[0] if len(handles) == 1 else None
-            if h is None:
-                import torch
-                bus = getattr(torch.cuda.get_device_properties(device_index), "pci_bus_id", None)
-                for c in handles:
-                    bdf = amdsmi.amdsmi_get_gpu_device_bdf(c)
-                    if bus is not None and int(bdf.split(":")[1], 16) == int(bus):
-                        h = c
-            if h is not None:
-                self._smi, self._h, self.source = amdsmi, h, "amd-smi gfx clock"
-        except Exception:
-            self._smi = None
-
-    def sample(self):
-        if self._smi is None:
-            return
-        try:
-            info = self._smi.amdsmi_get_clock_info(self._h, self._smi.AmdSmiClkType.GFX)
-            mhz = info.get("clk")
-            if isinstance(mhz, (int, float)) and mhz > 0:
-                self.samples.append(float(mhz))
-        except Exception:
-            self._smi = None
-
-    def summary(self):
-        if not self.samples:
-            return {"source": self.source or "unavailable", "samples": 0}
-        xs = sorted(self.samples)
-        return {"source": self.source, "samples": len(xs), "median_MHz": xs[len(xs) // 2],
-                "mean_MHz": round(sum(xs) / len(xs), 1), "min_MHz": xs[0], "max_MHz": xs[-1]}
 
 
 def cpu_baseline(w, q, k, v, descale, budget_s, dout=None):
@@ -363,22 +329,18 @@ def main():
     if bwd and w.dtype == "e4m3":
         print(json.dumps({"error": "the backward pass takes fp16 or bf16 inputs"}))
         sys.exit(2)
-    clock = ClockSampler()
-    rec = bench_dense(args, w, dev, bwd, clock=clock, cold_launches=args.cold_launches,
-                      cpu_seconds=args.cpu_baseline_seconds)
-    rec["clock"] = clock.summary()
+    rec = bench_dense(args, w, dev, bwd, cold_launches=args.cold_launches, cpu_seconds=args.cpu_baseline_seconds)
     if not bwd and args.workload == DEFAULT_WORKLOAD and args.bars:
         # the other configurations the throughput bars are stated on, measured in the same run
         rec["bars"] = {}
         for name in BAR_WORKLOADS:
-            bc = ClockSampler()
-            r = bench_dense(args, WORKLOADS[name], dev, False, clock=bc, cold_launches=0, cpu_seconds=0)
+            r = bench_dense(args, WORKLOADS[name], dev, False, cold_launches=0, cpu_seconds=0)
             rf = r["roofline"]
             rec["bars"][name] = {
                 "dtype": r["dtype"], "ms_per_step": r["ms_per_step"], "TFLOPs": r["value"],
                 "pct_of_mfma_peak": r["pct_of_mfma_peak"], "kernel_avg_us": rf["kernel_avg_us"],
                 "roofline": {key: rf[key] for key in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
-                "clock": bc.summary()}
+                "clock": r["clock"]}
     print(json.dumps(rec), flush=True)
 
 
@@ -388,7 +350,7 @@ BAR_WORKLOADS = ["causal_b4_h32_n4096_d64_bf16", "causal_fp8_b2_h32_n4096_d64_e4
                  "gqa_b1_hq32_hkv8_n16384_d128_bf16", "gqa_win256_b1_hq32_hkv8_n16384_d128_bf16"]
 
 
-def bench_dense(args, w, dev, bwd, clock=None, cold_launches=0, cpu_seconds=0.0):
+def bench_dense(args, w, dev, bwd, cold_launches=0, cpu_seconds=0.0):
     """One fa_fwd (or fa_bwd) workload in the timing protocol; returns its JSON record."""
     import torch
 
@@ -424,7 +386,7 @@ def bench_dense(args, w, dev, bwd, clock=None, cold_launches=0, cpu_seconds=0.0)
                 raise fa.FaError(st, fa.status_str(st))
 
     stream = torch.cuda.current_stream(dev)     # fa_fwd launches on this stream
-    ms_per_step, avg_kernel_s, med_kernel_s, tinfo = timed(step, args, stream, clock)
+    ms_per_step, avg_kernel_s, med_kernel_s, tinfo = timed(step, args, stream)
 
     # Cold-cache variant: 512 MiB written between launches evicts L2 and the MALL.
     cold = None
@@ -481,6 +443,7 @@ def bench_dense(args, w, dev, bwd, clock=None, cold_launches=0, cpu_seconds=0.0)
                                 "frac": round(gbs / HBM_PEAK_GBS, 4), "achieved_TFLOPs": round(achieved, 2),
                                 "frac_of_mfma_peak": round(achieved / peak, 4)})
     rec["timing"] = tinfo
+    rec["clock"] = committed_clock(("bwd_" if bwd else "") + w.name, "bwd" if bwd else "fwd")
     if cold is not None:
         rec["cold_cache"] = cold
     if bwd:
@@ -494,7 +457,7 @@ def bench_dense(args, w, dev, bwd, clock=None, cold_launches=0, cpu_seconds=0.0)
 PREHEAT_S = 0.25   # seconds of the step run before the timed region (engine clock ramp)
 
 
-def timed(step, args, stream, clock=None):
+def timed(step, args, stream):
     """The timing protocol of every bench line. W warm-up steps; K steps as a run that starts on an
     idle GPU sees them (reported as `unheated_ms_per_step`, not the value); the step repeated for
     PREHEAT_S seconds, because the engine clock rises over the first few tenths of a second under
@@ -522,17 +485,10 @@ def timed(step, args, stream, clock=None):
     pre = 0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    # launches per burst: about 10 ms of queued work, so that the clock is sampled while the GPU
-    # is busy (half way through each burst) rather than across the gaps between bursts
-    burst = max(4, int(0.010 / max(unheated_s / max(args.steps, 1), 1e-6)))
     while time.perf_counter() - t0 < PREHEAT_S:
-        tb = time.perf_counter()
-        for _ in range(burst):
+        for _ in range(4):
             step()
-        pre += burst
-        if clock is not None:
-            time.sleep(max(0.0, 0.005 - (time.perf_counter() - tb)))
-            clock.sample()
+        pre += 4
         torch.cuda.synchronize()
     wall, events_s = back_to_back(args.steps)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
