@@ -59,7 +59,7 @@ METRIC = "attention fwd TFLOP/s (4·B·H·Nq·Nk·D, causal halved) and % of MFM
 METRIC_BWD = "attention bwd TFLOP/s (2.5 x the forward FLOPs: five products of the forward's size)"
 BWD_FLOP_FACTOR = 2.5
 _CSRC = "exact_attention_09_amd/csrc/"
-_SHARED = ["fa_f16_common.hpp", "fa_device.hpp", "fa_mask.hpp", "fa_kernels.hpp", "fa355_api.hip"]
+_SHARED = ["fa_f16_common.hpp", "fa_device.hpp", "fa_mask.hpp", "fa_kernels.hpp", "fa_schedule.hpp", "fa355_api.hip"]
 # sources whose change makes a committed counter summary stale, per pass
 KERNEL_SOURCES = {
     "fwd": [_CSRC + f for f in ["fa_fwd_f16.hip", "fa_fwd_fp8.hip"] + _SHARED],

@@ -12,6 +12,7 @@
 
 #include "../../include/fa355.h"
 #include "fa_kernels.hpp"
+#include "fa_schedule.hpp"
 #include "fa_mask.hpp"
 
 namespace fa {
@@ -196,6 +197,17 @@ fa_status fa_kv_tile_range(int Nq, int Nk, int causal, int window_left, int wind
   if (full) *full = nf;
   if (partial) *partial = np;
   if (skipped) *skipped = ns;
+  return FA_OK;
+}
+
+fa_status fa_block_order(int64_t n, int num_tiles, int heads, int group, int causal, int packed, int* b, int* h,
+                         int* t) {
+  if (!b || !h || !t) return FA_ERR_NULL;
+  if (n < 1 || n >= ((int64_t)1 << 31) || num_tiles < 1 || heads < 1 || group < 1 || heads % group != 0 ||
+      n % ((int64_t)heads * num_tiles) != 0)
+    return FA_ERR_SHAPE;
+  for (int id = 0; id < (int)n; ++id)
+    fa::schedule_block(id, (int)n, num_tiles, heads, group, causal != 0, packed != 0, &b[id], &h[id], &t[id]);
   return FA_OK;
 }
 

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_schedule.hpp"
+
 namespace fa {
 
 // f(Int<0>{}), ..., f(Int<N-1>{}): a loop whose index is a compile-time constant in every trip
@@ -36,58 +38,6 @@ constexpr float kLn2 = 0.69314718055994530942f;
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
-}
-
-// Block index -> logical block index, so that each XCD's share is one contiguous range.
-__device__ inline int xcd_remap(int id, int n) {
-  const int xcd = id & 7, k = id >> 3;
-  const int per = n >> 3, rem = n & 7;
-  return xcd * per + (xcd < rem ? xcd : rem) + k;
-}
-
-// Which (batch, head, tile) workgroup `id` of a launch of n = (batch x heads) x num_tiles
-// computes. Heads are enumerated batch-major (inside a batch the query heads sharing a K/V head
-// are consecutive); under a causal mask tile t is the longest of its head when t = num_tiles - 1
-// and the shortest when t = 0. Blocks are dealt round-robin over the 8 XCDs.
-//  * No causal mask: head by head, each XCD one contiguous range of heads (xcd_remap), so a
-//    head's K/V stays in one XCD's L2.
-//  * Causal, heads a multiple of 8: each XCD takes a contiguous range of whole heads and goes
-//    through them by chunks of up to kChunk heads (a divisor of its head count; one K/V head
-//    under 4-way GQA), longest tiles of the chunk first: the chunk in flight keeps the XCD's L2
-//    working set small, every XCD gets the same mix of long and short tiles, and the longest
-//    work starts first, which keeps the launch's tail short.
-//  * Causal otherwise, and packed batches of sequences of different lengths (`spread`: whole
-//    sequences on one XCD would leave the XCDs unequally loaded): highest tiles of every head
-//    first, consecutive ids on different XCDs.
-__device__ inline void schedule_block(int id, int n, int num_tiles, int H, bool causal, int* b, int* h, int* t,
-                                      bool spread = false) {
-  constexpr int kChunk = 4;
-  const int n_bh = n / num_tiles;
-  int bh;
-  if (spread) {
-    const int rank = id / n_bh;
-    bh = id - rank * n_bh;
-    *t = num_tiles - 1 - rank;
-  } else if (!causal) {
-    const int L = xcd_remap(id, n);
-    bh = L / num_tiles;
-    *t = L - bh * num_tiles;
-  } else if (n_bh % 8 == 0) {
-    const int hx = n_bh / 8;   // heads per XCD
-    const int c = hx % kChunk == 0 ? kChunk : (hx % 2 == 0 ? 2 : 1);
-    const int L = xcd_remap(id, n);
-    const int per = c * num_tiles;
-    const int chunk = L / per, r = L - chunk * per;
-    const int rank = r / c;
-    bh = chunk * c + (r - rank * c);
-    *t = num_tiles - 1 - rank;
-  } else {
-    const int rank = id / n_bh;
-    bh = id - rank * n_bh;
-    *t = num_tiles - 1 - rank;
-  }
-  *b = bh / H;
-  *h = bh - *b * H;
 }
 
 // Value of x held by lane l ^ 32, combined with x: max or sum over the lane pair.

@@ -22,7 +22,7 @@ _OUT_DTYPE = {FA_F16: torch.float16, FA_BF16: torch.bfloat16, FA_FP8_E4M3: torch
 # Every symbol include/fa355.h declares.
 EXPORTED = ("fa_fwd", "fa_fwd_blocksparse", "fa_fwd_varlen", "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_bytes",
             "fa_fwd_kvcache_noalloc", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_str", "fa_fwd_plan",
-            "fa_kv_tile_range", "fa_version")
+            "fa_kv_tile_range", "fa_block_order", "fa_version")
 # FA_NOALLOC_SCRATCH_BYTES of include/fa355.h: the fixed per-device scratch of fa_fwd_kvcache_noalloc.
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -94,6 +94,8 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_plan.argtypes = [c_int] * 10 + [ctypes.POINTER(FaPlanInfo)]
     lib.fa_kv_tile_range.restype = c_int
     lib.fa_kv_tile_range.argtypes = [c_int] * 8 + [ctypes.POINTER(c_int)] * 5
+    lib.fa_block_order.restype = c_int
+    lib.fa_block_order.argtypes = [ctypes.c_int64] + [c_int] * 5 + [ctypes.c_void_p] * 3
     lib.fa_version.restype = c_int
     lib.fa_version.argtypes = []
     _lib = lib
@@ -400,6 +402,17 @@ def kv_tile_range(Nq, Nk, causal, window, block_n, row_begin, row_end):
     if st != 0:
         raise FaError(st, status_str(st))
     return tuple(x.value for x in vals)
+
+
+def block_order(n, num_tiles, heads, group=1, causal=False, packed=False):
+    """(b, h, t) int32 numpy arrays: the (batch, head, query tile) of workgroups 0 .. n-1 of a launch."""
+    import numpy as np
+    b, h, t = (np.empty(n, dtype=np.int32) for _ in range(3))
+    st = load().fa_block_order(n, num_tiles, heads, group, int(bool(causal)), int(bool(packed)), b.ctypes.data,
+                               h.ctypes.data, t.ctypes.data)
+    if st != 0:
+        raise FaError(st, status_str(st))
+    return b, h, t
 
 
 def bwd_raw(q, k, v, out, dout, lse, dq, dk, dv, workspace, causal=False, window=(-1, -1), softmax_scale=None,

@@ -307,6 +307,19 @@ fa_status fa_kv_tile_range(int Nq, int Nk, int causal, int window_left, int wind
                            int block_n, int row_begin, int row_end, int* tile_begin, int* tile_end,
                            int* full, int* partial, int* skipped);
 
+/*
+ * fa_block_order — for each workgroup id 0 .. n-1 of a forward launch of n = batches * heads *
+ * num_tiles workgroups, the (batch, head, query tile) it computes: the order in which the
+ * kernels visit their work, which decides which XCD (id % 8) and which L2 reads a head's K/V and
+ * when. Host only, no device call. heads: query heads per batch; group: query heads per K/V
+ * head; causal: nonzero for a causal launch; packed: nonzero for a fa_fwd_varlen launch. b, h, t:
+ * host arrays of n ints, written. Returns FA_ERR_NULL for a null array, FA_ERR_SHAPE unless
+ * n, num_tiles, heads and group are >= 1, heads % group == 0, n % (heads * num_tiles) == 0 and
+ * n < 2^31.
+ */
+fa_status fa_block_order(int64_t n, int num_tiles, int heads, int group, int causal, int packed, int* b, int* h,
+                         int* t);
+
 /* Library version, major * 10000 + minor * 100 + patch. */
 int fa_version(void);
 

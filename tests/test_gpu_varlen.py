@@ -44,6 +44,9 @@ MIXES = [
     ([300, 0, 45, 260], [300, 12, 45, 0], 4, 2, 128, True, (37, 11)),  # empty queries, keys-less rows
     ([640, 7, 384], None, 2, 2, 64, False, (100, 100)),
     ([190, 190, 190], None, 6, 3, 128, True, (64, -1)),
+    # 8 K/V heads per sequence: the launch deals K/V heads over the XCDs by chunks of query heads
+    ([300, 1000, 77, 512], None, 16, 8, 64, True, (-1, -1)),
+    ([129, 640], None, 8, 8, 128, False, (-1, -1)),
 ]
 
 
@@ -77,19 +80,29 @@ def test_varlen_equal_lengths_bitwise_dense(dtype):
 
 @pytest.mark.parametrize("name", list(VARLEN_WORKLOADS))
 def test_varlen_benchmark_workload_sampled(name):
-    """The benchmark's packed batches in the launch it times: the first and last 16 rows of every
-    sequence, for two heads, against the oracle of that sequence alone (reading RV1: a packed
-    sequence is the dense problem of its own lengths; the dense oracle's row sampler)."""
+    """The benchmark's packed batches in the launch it times, written into NaN-filled outputs: every
+    element is written, and the first and last 16 rows of every sequence (heads 0 and Hq-1) and
+    the first and last 4 rows (every other head) match the oracle of that sequence alone (reading
+    RV1: a packed sequence is the dense problem of its own lengths; the dense oracle's row
+    sampler)."""
     w = VARLEN_WORKLOADS[name]
     lens = w.lengths(0)
     q, k, v, cu_q, cu_k, d = make_varlen_inputs(lens, lens, w.Hq, w.Hkv, w.D, w.dtype, seed=0)
-    out, lse = run(q, k, v, cu_q, cu_k, max(lens), w.causal, w.window, w.softmax_scale(), d)
-    assert torch.isfinite(out.float()).all()
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    out = torch.full(q.shape, float("nan"), dtype=torch.float16 if w.dtype == "f16" else torch.bfloat16,
+                     device="cuda")
+    lse = torch.full((w.Hq, q.shape[0]), float("nan"), dtype=torch.float32, device="cuda")
+    st = fa.fwd_varlen_raw(qd, kd, vd, out, lse, cu_q.cuda(), cu_k.cuda(), max(lens), w.causal, w.window,
+                           w.softmax_scale(), d)
+    torch.cuda.synchronize()
+    assert st == 0, fa.status_str(st)
+    out, lse = out.cpu(), lse.cpu()
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
     G = w.Hq // w.Hkv
     for b, n in enumerate(lens):
         s = int(cu_q[b])
-        rows = np.r_[0:16, n - 16:n]
-        for h in (0, w.Hq - 1):
+        for h in range(w.Hq):
+            rows = np.r_[0:16, n - 16:n] if h in (0, w.Hq - 1) else np.r_[0:4, n - 4:n]
             g = h // G
             qh = decode(q[s:s + n, h])[None, :, None, :]
             kh = decode(k[s:s + n, g])[None, :, None, :]
