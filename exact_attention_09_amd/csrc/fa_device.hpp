@@ -80,9 +80,11 @@ __device__ inline BufDesc desc_at(const BufDesc& d, uint32_t off) {
   off = __builtin_amdgcn_readfirstlane(off);
   const uint64_t a = (((uint64_t)(d.w[1] & 0xFFFFu) << 32) | d.w[0]) + off;
   // max(bytes, off) - off on the scalar unit (written as a select, the compiler picks a clamped
-  // vector subtract and a readfirstlane)
+  // vector subtract and a readfirstlane). s_max_u32 writes SCC: the clobber keeps the compiler
+  // from placing it inside a carry chain (between the s_add_u32 and s_addc_u32 of the base
+  // address above), where it would corrupt the carry into the high address bits.
   uint32_t hi;
-  asm("s_max_u32 %0, %1, %2" : "=s"(hi) : "s"(d.w[2]), "s"(off));
+  asm("s_max_u32 %0, %1, %2" : "=s"(hi) : "s"(d.w[2]), "s"(off) : "scc");
   const uint32_t n = hi - off;
   auto u = [](uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane(x); };
   return BufDesc{{u((uint32_t)a), u((d.w[1] & 0xFFFF0000u) | ((uint32_t)(a >> 32) & 0xFFFFu)), u(n), d.w[3]}};
