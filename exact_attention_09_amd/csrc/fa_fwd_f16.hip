@@ -218,11 +218,12 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   // finite value rather than -inf: the first tile with an admitted key then overflows the sum
   // bound and sets the reference (see kSumBound), while a fully masked tile still gives
   // p = exp2(-inf) = 0.
+  constexpr float kRefStart = -1e30f;
   float m[QB], l[QB];    // l: this lane's share of the running sum (lanes l, l^32 split the keys)
   f32x16 o[QB][DB];
 #pragma unroll
   for (int qb2 = 0; qb2 < QB; ++qb2) {
-    m[qb2] = -1e30f;
+    m[qb2] = kRefStart;
     l[qb2] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[qb2][db] = f32x16{};
@@ -380,6 +381,26 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
         }
       } else {
         if (!((uint32_t)(j - flo) < full_n)) mask_tile(sc, j);
+      }
+      // A row's first tile with an admitted key would trip the sum bound (its reference is still
+      // the start value) and pay a second softmax pass in check_rebase; the row's reference is
+      // set from this tile's max instead. Nothing has been accumulated for such a row (l = 0,
+      // O = 0), so no rescale is due; a row whose keys in this tile are all masked keeps the
+      // start value. A row's first admitted key grows with the row, so over the wave's 32 * QB
+      // rows it spans at most 32 * QB keys: QB + 1 tiles from the wave's first. Only those steps
+      // look; a row first admitted later (the check is an optimisation) goes through
+      // check_rebase as before.
+#pragma unroll
+      for (int qb2 = 0; qb2 < QB; ++qb2) {
+        if ((SP || (uint32_t)(j - jlo) <= (uint32_t)QB) && __builtin_amdgcn_ballot_w64(m[qb2] == kRefStart)) {
+          float mx = sc[qb2][0][0];
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[qb2][kb][r]);
+          const float mt = pair_max(mx) * c2;
+          if (m[qb2] == kRefStart) m[qb2] = fmaxf(kRefStart, mt);
+        }
       }
       // Operand u of the step (even u: K operand u / 2, read by rows from LDS; odd u: V^T
       // operand u / 2, read by transpose reads), read PF operands ahead of its first use. At
