@@ -206,8 +206,8 @@ fa_status fa_block_order(int64_t n, int num_tiles, int heads, int group, int cau
   if (n < 1 || n >= ((int64_t)1 << 31) || num_tiles < 1 || heads < 1 || group < 1 || heads % group != 0 ||
       n % ((int64_t)heads * num_tiles) != 0)
     return FA_ERR_SHAPE;
-  for (int id = 0; id < (int)n; ++id)
-    fa::schedule_block(id, (int)n, num_tiles, heads, group, causal != 0, packed != 0, &b[id], &h[id], &t[id]);
+  const fa::Schedule S = fa::make_schedule((int)n, num_tiles, heads, group, causal != 0, packed != 0);
+  for (int id = 0; id < (int)n; ++id) fa::schedule_block(id, S, &b[id], &h[id], &t[id]);
   return FA_OK;
 }
 
@@ -305,6 +305,7 @@ fa_status fwd_impl(const void* q, const void* k, const void* v, void* out, float
       fa::tile_shape(D, dtype, fa::short_rows(D, dtype, causal, window_left, window_right, sparse), sparse);
   a.num_q_tiles = (Nq + ts.block_m - 1) / ts.block_m;
   const int64_t grid = (int64_t)B * Hq * a.num_q_tiles;
+  a.sched = fa::make_schedule((int)grid, a.num_q_tiles, Hq, a.group, causal != 0, false);
   const hipError_t e = fa::launch_fwd(a, D, dtype, ts, grid, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -399,6 +400,7 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, 
       fa::tile_shape(D, dtype, fa::short_rows(D, dtype, causal, window_left, window_right, false), false);
   a.num_q_tiles = (max_seqlen_q + ts.block_m - 1) / ts.block_m;
   const int64_t grid = (int64_t)B * Hq * a.num_q_tiles;
+  a.sched = fa::make_schedule((int)grid, a.num_q_tiles, Hq, a.group, causal != 0, true);
   const hipError_t e = fa::launch_fwd(a, D, dtype, ts, grid, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -580,6 +582,9 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* out, c
   if ((int64_t)B * Hkv * a.num_k_tiles * a.n_split >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
   a.scale = softmax_scale;
   a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  a.sched_q = fa::make_schedule((int)((int64_t)B * Hq * a.num_q_tiles), a.num_q_tiles, Hq, 1, causal != 0, false);
+  a.sched_k = fa::make_schedule((int)((int64_t)B * Hkv * a.n_split * a.num_k_tiles), a.num_k_tiles, Hkv * a.n_split, 1,
+                                causal != 0, false);
   const hipError_t e = fa::launch_bwd(a, D, dtype, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

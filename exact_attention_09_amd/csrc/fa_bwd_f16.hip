@@ -101,7 +101,7 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int b, h, qt;
-  schedule_block(blockIdx.x, gridDim.x, a.num_q_tiles, a.Hq, 1, a.causal != 0, false, &b, &h, &qt);
+  schedule_block(blockIdx.x, a.sched_q, &b, &h, &qt);
   const int hk = h / a.group;
   const int q0 = qt * BM;
   const MaskSpec ms{a.Nq, a.Nk, a.causal, a.wl, a.wr};
@@ -279,7 +279,7 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
   // (batch, K/V head, split of its query heads, key tile) in the forward kernel's launch order,
   // longest work first under a causal mask: there the first key tiles meet the most query tiles
   int b, hs, kt;
-  schedule_block(blockIdx.x, gridDim.x, a.num_k_tiles, a.Hkv * a.n_split, 1, a.causal != 0, false, &b, &hs, &kt);
+  schedule_block(blockIdx.x, a.sched_k, &b, &hs, &kt);
   kt = a.num_k_tiles - 1 - kt;
   const int hk = hs / a.n_split, sp = hs - hk * a.n_split;
   const int gq = a.group / a.n_split;   // query heads of this workgroup: hk * group + sp * gq + 0 .. gq-1

@@ -74,8 +74,8 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
 
   // ---- which (batch, head, query tile) this workgroup computes
   int b, h, qt;
-  schedule_block(blockIdx.x, gridDim.x, a.num_q_tiles, a.Hq, a.group, a.causal != 0, a.cu_q != nullptr, &b, &h, &qt);
-  const int hk = h / a.group;                    // MQA/GQA: K/V head of this query head
+  schedule_block(blockIdx.x, a.sched, &b, &h, &qt);
+  const int hk = (int)fdiv((uint32_t)h, a.sched.group);   // MQA/GQA: K/V head of this query head
   const int q0 = qt * BM;
   const SeqView sv = seq_view(a, b, h, D, ES, ES);
   if (q0 >= sv.Nq) return;                       // past the end of a shorter packed sequence
@@ -98,31 +98,9 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   const int w0 = q0 + wave * WR;
   const bool wave_live = w0 < sv.Nq;
   const int w1 = min(w0 + WR - 1, sv.Nq - 1);
-  // Key bounds of the wave's first and last rows, clamped to [-1, Nk] (wave-uniform scalars).
-  // Each row admits an interval of keys and both ends grow with the row, so the tiles holding
-  // an admitted key for some row of the wave form an interval [jlo, jhi), and the tiles admitted
-  // for every row another one, [flo, fhi), inside it.
-  auto clamp_key = [&](int64_t x) { return (int)(x < -1 ? -1 : (x > sv.Nk ? sv.Nk : x)); };
-  const int wlo0 = __builtin_amdgcn_readfirstlane(clamp_key(key_lo(ms, w0)));
-  const int wlo1 = __builtin_amdgcn_readfirstlane(clamp_key(key_lo(ms, w1)));
-  const int whi0 = __builtin_amdgcn_readfirstlane(clamp_key(key_hi(ms, w0)));
-  const int whi1 = __builtin_amdgcn_readfirstlane(clamp_key(key_hi(ms, w1)));
-  int jlo = 0, jhi = 0;
-  if (wave_live && whi1 >= wlo0) {
-    jlo = max(tb, wlo0 / BN);
-    jhi = min(te, whi1 / BN + 1);
-  }
-  const int flo = (wlo1 + BN - 1) / BN, fhi = (whi0 + 1) / BN;
-  // this lane's query row in each block, and the keys it admits: [lo_i, lo_i + span_i)
-  int my_row[QB], lo_i[QB];
-  uint32_t span_i[QB];
+  int my_row[QB];   // this lane's query row in each block
 #pragma unroll
-  for (int qb2 = 0; qb2 < QB; ++qb2) {
-    my_row[qb2] = w0 + qb2 * 32 + l32;
-    lo_i[qb2] = clamp_key(key_lo(ms, my_row[qb2]));
-    const int hi_i = clamp_key(key_hi(ms, my_row[qb2]));
-    span_i[qb2] = hi_i >= lo_i[qb2] ? (uint32_t)(hi_i - lo_i[qb2] + 1) : 0u;
-  }
+  for (int qb2 = 0; qb2 < QB; ++qb2) my_row[qb2] = w0 + qb2 * 32 + l32;
 
   // ---- block-sparse: the tiles of [tb, te) that the block mask sets for one of the workgroup's
   // mask rows, compacted into LDS by wave 0 (sp_list: tile ids, then a bit per mask row, then the
@@ -198,6 +176,48 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
+
+  // ---- prologue loads, issued before the rest of the set-up so that their latency overlaps it:
+  // K(tb), K(tb+1), V(tb), K(tb+2) (positions 0, 1, 2 of the tile list when block-sparse) into
+  // ring slots 0, 1, 0, 2, and this wave's Q rows
+  if (pb0 < pe) {
+    const int t0 = SP ? sp_tile(0) : tb, t1 = SP ? sp_tile(1) : tb + 1, t2 = SP ? sp_tile(2) : tb + 2;
+    dma(k_d, kgoff, (uint32_t)(t0 * BN) * k_rowb, kring_a);
+    if (pb0 + 1 < pe) dma(k_d, kgoff, (uint32_t)(t1 * BN) * k_rowb, kring_a + TILEB);
+    dma(v_d, vgoff, (uint32_t)(t0 * BN) * v_rowb, vring_a);
+    if (pb0 + 2 < pe) dma(k_d, kgoff, (uint32_t)(t2 * BN) * k_rowb, kring_a + 2 * TILEB);
+  }
+#pragma unroll
+  for (int qb2 = 0; qb2 < QB; ++qb2)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qop[qb2][ks] = __builtin_amdgcn_raw_buffer_load_b128(q_r, (uint32_t)my_row[qb2] * q_rowb + (ks * 16 + hl * 8) * ES,
+                                                           0, 0);
+
+  // Key bounds of the wave's first and last rows, clamped to [-1, Nk] (wave-uniform scalars).
+  // Each row admits an interval of keys and both ends grow with the row, so the tiles holding
+  // an admitted key for some row of the wave form an interval [jlo, jhi), and the tiles admitted
+  // for every row another one, [flo, fhi), inside it.
+  auto clamp_key = [&](int64_t x) { return (int)(x < -1 ? -1 : (x > sv.Nk ? sv.Nk : x)); };
+  const int wlo0 = __builtin_amdgcn_readfirstlane(clamp_key(key_lo(ms, w0)));
+  const int wlo1 = __builtin_amdgcn_readfirstlane(clamp_key(key_lo(ms, w1)));
+  const int whi0 = __builtin_amdgcn_readfirstlane(clamp_key(key_hi(ms, w0)));
+  const int whi1 = __builtin_amdgcn_readfirstlane(clamp_key(key_hi(ms, w1)));
+  int jlo = 0, jhi = 0;
+  if (wave_live && whi1 >= wlo0) {
+    jlo = max(tb, wlo0 / BN);
+    jhi = min(te, whi1 / BN + 1);
+  }
+  const int flo = (wlo1 + BN - 1) / BN, fhi = (whi0 + 1) / BN;
+  // the keys this lane's row in each block admits: [lo_i, lo_i + span_i)
+  int lo_i[QB];
+  uint32_t span_i[QB];
+#pragma unroll
+  for (int qb2 = 0; qb2 < QB; ++qb2) {
+    lo_i[qb2] = clamp_key(key_lo(ms, my_row[qb2]));
+    const int hi_i = clamp_key(key_hi(ms, my_row[qb2]));
+    span_i[qb2] = hi_i >= lo_i[qb2] ? (uint32_t)(hi_i - lo_i[qb2] + 1) : 0u;
+  }
 
   // Per-lane LDS offsets. K (A operand of S^T): row kb*32 + l32, chunk 2*ks + hl.
   int koff[KS];
@@ -323,21 +343,6 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   // it: zero it so that the product is exactly zero.
 #pragma unroll
   for (int c = tid * 16; c < TILEB; c += NT * 16) *(i32x4*)(vring + 2 * TILEB + c) = i32x4{};
-  // prologue: K(tb), K(tb+1), V(tb), K(tb+2) in flight; K(tb) and K(tb+1) landed; S(tb)
-  // (positions 0, 1, 2 of the tile list when block-sparse)
-  if (pb0 < pe) {
-    const int t0 = SP ? sp_tile(0) : tb, t1 = SP ? sp_tile(1) : tb + 1, t2 = SP ? sp_tile(2) : tb + 2;
-    dma(k_d, kgoff, (uint32_t)(t0 * BN) * k_rowb, kring_a);
-    if (pb0 + 1 < pe) dma(k_d, kgoff, (uint32_t)(t1 * BN) * k_rowb, kring_a + TILEB);
-    dma(v_d, vgoff, (uint32_t)(t0 * BN) * v_rowb, vring_a);
-    if (pb0 + 2 < pe) dma(k_d, kgoff, (uint32_t)(t2 * BN) * k_rowb, kring_a + 2 * TILEB);
-  }
-#pragma unroll
-  for (int qb2 = 0; qb2 < QB; ++qb2)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qop[qb2][ks] = __builtin_amdgcn_raw_buffer_load_b128(q_r, (uint32_t)my_row[qb2] * q_rowb + (ks * 16 + hl * 8) * ES,
-                                                           0, 0);
   // Q (and with it the first tiles) must have landed before the pipelined loop: without this
   // wait the compiler's wait-count analysis, merging the loop back edge, would make every
   // iteration wait on the prefetches.

@@ -95,8 +95,8 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_fp8_kernel(FwdArgs a) {
 
   // which (batch, head, query tile) this workgroup computes
   int b, h, qt;
-  schedule_block(blockIdx.x, gridDim.x, a.num_q_tiles, a.Hq, a.group, a.causal != 0, a.cu_q != nullptr, &b, &h, &qt);
-  const int hk = h / a.group;
+  schedule_block(blockIdx.x, a.sched, &b, &h, &qt);
+  const int hk = (int)fdiv((uint32_t)h, a.sched.group);
   const int q0 = qt * BM;
   const SeqView sv = seq_view(a, b, h, D, 1, 2);
   if (q0 >= sv.Nq) return;                       // past the end of a shorter packed sequence

@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "fa_schedule.hpp"
+
 namespace fa {
 
 // Everything one launch needs; passed by value as the kernel argument.
@@ -35,6 +37,7 @@ struct FwdArgs {
   // the query head.
   const uint8_t* block_mask;
   int mask_heads, nqb, nkb;
+  Schedule sched;        // the launch order (make_schedule over the grid, num_q_tiles, Hq, group)
 };
 constexpr int kSparseBlockQ = 128;
 constexpr int kSparseBlockK = 64;
@@ -107,6 +110,8 @@ struct BwdArgs {
   uint32_t q_bytes, k_bytes, v_bytes, o_bytes, do_bytes, dq_bytes, dk_bytes, dv_bytes;
   float scale;           // softmax_scale
   float scale_log2;      // softmax_scale * log2(e)
+  Schedule sched_q;      // launch order of the dq kernel: its grid, num_q_tiles, Hq
+  Schedule sched_k;      // of the dk/dv kernel: its grid, num_k_tiles, Hkv * n_split
 };
 
 // Queries against a dense or paged key/value cache (decode-shaped: few queries, long keys), split

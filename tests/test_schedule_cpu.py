@@ -103,3 +103,46 @@ def test_rejects_bad_shapes(args):
     n, tiles, heads, group = args
     with pytest.raises(fa.FaError):
         fa.block_order(n, tiles, heads, group)
+
+
+def expected_order(B, H, group, tiles, causal, packed):
+    """The launch order written out with plain integer division (the rules the kernels follow)."""
+    n = B * H * tiles
+    n_bh = B * H
+    hx = n_bh // 8
+    c = 4 if hx % 4 == 0 else (2 if hx % 2 == 0 else 1)
+
+    def xcd_remap(i):
+        x, k = i & 7, i >> 3
+        per, rem = n >> 3, n & 7
+        return x * per + min(x, rem) + k
+
+    out = []
+    for i in range(n):
+        if packed and (H // group) % 8 == 0:
+            x, k = i & 7, i >> 3
+            chunk, r = divmod(k, c * tiles)
+            rank, pi = r // c, chunk * c + r % c
+            bh = ((pi // group) * 8 + x) * group + pi % group
+            t = tiles - 1 - rank
+        elif packed or (causal and n_bh % 8):
+            rank, bh = divmod(i, n_bh)
+            t = tiles - 1 - rank
+        elif not causal:
+            bh, t = divmod(xcd_remap(i), tiles)
+        else:
+            chunk, r = divmod(xcd_remap(i), c * tiles)
+            rank = r // c
+            bh, t = chunk * c + r % c, tiles - 1 - rank
+        out.append((bh // H, bh % H, t))
+    return out
+
+
+@pytest.mark.parametrize("case", CASES + [(7, 24, 3, 11, True, False), (9, 16, 2, 13, False, True),
+                                          (2, 48, 6, 5, True, True), (1, 8, 1, 1, True, False)],
+                         ids=lambda c: "B{}_H{}_g{}_t{}_c{}_p{}".format(*map(int, c)))
+def test_matches_plain_division(case):
+    """The kernels divide by launch constants with host-computed multipliers; the order must be the
+    one plain integer division gives."""
+    b, h, t = order(*case)
+    assert list(zip(b.tolist(), h.tolist(), t.tolist())) == expected_order(*case)
