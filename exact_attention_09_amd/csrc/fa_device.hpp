@@ -126,6 +126,7 @@ __device__ inline void dma4(const BufDesc& d0, uint32_t voff, uint32_t soff, uin
 typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 __device__ inline i32x4 lds_read_b128(uint32_t addr) { return *(const lds_i32x4*)(uintptr_t)addr; }
+__device__ inline void lds_write_b64(uint32_t addr, i32x2 v) { *(lds_i32x2*)(uintptr_t)addr = v; }
 __device__ inline i32x2 lds_read_tr16(uint32_t addr) {
   return __builtin_bit_cast(i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(uintptr_t)addr));
 }

@@ -486,10 +486,19 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
 
   // ---- epilogue: O / l, lse = (m + log2 l) * ln 2
   if (!wave_live) return;
+  // O leaves through LDS: each wave writes one 32-row block of its output there in the MFMA
+  // layout (8 bytes per lane and row) and reads it back by rows, so that each store writes whole
+  // rows (64 lanes x 16 bytes) instead of 16 bytes in each of 32 rows. The rings are free: the
+  // last step's barrier follows every wave's last LDS read and load. Each wave has its own
+  // 32 * ROWB-byte region; 16-byte chunk c of row r sits at chunk c ^ (r % CPR), so neither the
+  // column-wise writes nor the row-wise reads meet bank conflicts. Rows past the sequence are
+  // written to LDS and then dropped by the buffer range check of their stores.
+  static_assert(WAVES * 32 * ROWB <= 2 * NS * TILEB, "the output stage fits in the rings");
+  constexpr int RPI = 1024 / ROWB;   // rows one 64-lane, 16-byte access covers
+  const uint32_t stage = lds_addr_of(smem) + wave * 32 * ROWB;
 #pragma unroll
   for (int qb2 = 0; qb2 < QB; ++qb2) {
     const float l_tot = pair_sum(l[qb2]);
-    if (my_row[qb2] >= sv.Nq) continue;
     const float inv = l_tot > 0.f ? a.out_scale / l_tot : 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -497,10 +506,17 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
       for (int q4 = 0; q4 < 4; ++q4) {
         const uint32_t w0v = TR::pack(o[qb2][db][4 * q4 + 0] * inv, o[qb2][db][4 * q4 + 1] * inv);
         const uint32_t w1v = TR::pack(o[qb2][db][4 * q4 + 2] * inv, o[qb2][db][4 * q4 + 3] * inv);
-        __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)w0v, (int)w1v}, o_r,
-                                              (uint32_t)my_row[qb2] * o_rowb + (db * 32 + q4 * 8 + hl * 4) * ES, 0, 0);
+        lds_write_b64(stage + l32 * ROWB + (((db * 4 + q4) ^ (l32 % CPR)) << 4) + hl * 8, i32x2{(int)w0v, (int)w1v});
       }
-    if (a.lse != nullptr && hl == 0) {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the reads below follow the writes (one wave: in order)
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = i * RPI + lane / CPR, c = lane % CPR;
+      const i32x4 v = lds_read_b128(stage + r * ROWB + ((c ^ (r % CPR)) << 4));
+      __builtin_amdgcn_raw_buffer_store_b128(v, o_r, (uint32_t)(w0 + qb2 * 32 + r) * o_rowb + c * 16, 0, 0);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the next block's writes follow these reads
+    if (a.lse != nullptr && hl == 0 && my_row[qb2] < sv.Nq) {
       const float lse = l_tot > 0.f ? (m[qb2] + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
       a.lse[sv.lse0 + my_row[qb2]] = lse;
     }
