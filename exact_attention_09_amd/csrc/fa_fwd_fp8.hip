@@ -352,7 +352,14 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_fp8_kernel(FwdArgs a) {
   }
 
   // epilogue: O * dv / l (both carry the 2^8 shift), lse = (m + log2(l / 2^8)) * ln 2
-  if (!wave_live || my_row >= sv.Nq) return;
+  if (!wave_live) return;
+  // O (bf16) leaves through LDS as in the fp16/bf16 kernel: each wave writes its 32 rows into a
+  // private region of the idle rings in the MFMA layout and stores them back by whole rows
+  // (16-byte chunk c of row r at c ^ (r % OCPR)); rows past the sequence are dropped by the
+  // buffer range check.
+  constexpr int OROWB = D * 2, OCPR = OROWB / 16, RPI = 1024 / OROWB;
+  static_assert(WAVES * 32 * OROWB <= 2 * NS * TILEB, "the output stage fits in the rings");
+  const uint32_t stage = lds_addr_of(smem) + wave * 32 * OROWB;
   const float l_tot = pair_sum(l);
   const float inv = l_tot > 0.f ? a.out_scale / l_tot : 0.f;
 #pragma unroll
@@ -363,10 +370,16 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_fp8_kernel(FwdArgs a) {
                                                                (__bf16)(o[db][4 * q4 + 1] * inv)});
       const uint32_t w1v = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)(o[db][4 * q4 + 2] * inv),
                                                                (__bf16)(o[db][4 * q4 + 3] * inv)});
-      __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)w0v, (int)w1v}, o_r,
-                                            (uint32_t)my_row * o_rowb + (db * 32 + q4 * 8 + hl * 4) * 2, 0, 0);
+      lds_write_b64(stage + l32 * OROWB + (((db * 4 + q4) ^ (l32 % OCPR)) << 4) + hl * 8, i32x2{(int)w0v, (int)w1v});
     }
-  if (a.lse != nullptr && hl == 0) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the reads below follow the writes (one wave: in order)
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / OCPR, c = lane % OCPR;
+    const i32x4 v = lds_read_b128(stage + r * OROWB + ((c ^ (r % OCPR)) << 4));
+    __builtin_amdgcn_raw_buffer_store_b128(v, o_r, (uint32_t)(w0 + r) * o_rowb + c * 16, 0, 0);
+  }
+  if (a.lse != nullptr && hl == 0 && my_row < sv.Nq) {
     const float lse = l_tot > 0.f ? (m - kPShiftLog2 + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
     a.lse[sv.lse0 + my_row] = lse;
   }
