@@ -246,7 +246,17 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(BwdArgs a) {
     s = s == (NSL - 1) * TILEB ? 0 : s + TILEB;
   }
 
-  if (!wave_live || my_row >= a.Nq) return;
+  // dq leaves through LDS (as the forward's output): every wave is past its last read of the
+  // rings after this barrier; each wave writes its 32 rows into a private region in the MFMA
+  // layout (16-byte chunk c of row r at c ^ (r % CPR)) and stores them by whole rows; rows past
+  // Nq are dropped by the buffer range check.
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (!wave_live) return;
+  constexpr int OROWB = D * ES, CPR = OROWB / 16, RPI = 1024 / OROWB;
+  static_assert(4 * 32 * OROWB <= 2 * NSL * TILEB, "the output stage fits in the rings");
+  const uint32_t stage = lds_addr_of(smem) + wave * 32 * OROWB;
   const uint32_t dq_rowb = (uint32_t)(a.dq_n * ES);
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -254,9 +264,15 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(BwdArgs a) {
     for (int q4 = 0; q4 < 4; ++q4) {
       const uint32_t w0v = TR::pack(dq[db][4 * q4 + 0] * a.scale, dq[db][4 * q4 + 1] * a.scale);
       const uint32_t w1v = TR::pack(dq[db][4 * q4 + 2] * a.scale, dq[db][4 * q4 + 3] * a.scale);
-      __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)w0v, (int)w1v}, dq_r,
-                                            (uint32_t)my_row * dq_rowb + (db * 32 + q4 * 8 + hl * 4) * ES, 0, 0);
+      lds_write_b64(stage + l32 * OROWB + (((db * 4 + q4) ^ (l32 % CPR)) << 4) + hl * 8, i32x2{(int)w0v, (int)w1v});
     }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the reads below follow the writes (one wave: in order)
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / CPR, c = lane % CPR;
+    const i32x4 v = lds_read_b128(stage + r * OROWB + ((c ^ (r % CPR)) << 4));
+    __builtin_amdgcn_raw_buffer_store_b128(v, dq_r, (uint32_t)(w0 + r) * dq_rowb + c * 16, 0, 0);
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -565,8 +581,8 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
     s = s == 2 * TILEB ? 0 : s + TILEB;
   }
 
-  if (my_key >= a.Nk) return;
   if (a.n_split > 1) {
+    if (my_key >= a.Nk) return;
     // fp32 partial sums; fa_bwd_reduce_kernel adds the splits and scales dk
     const int64_t slab = (int64_t)a.n_split * a.B * a.Hkv * a.Nk * D;
     float* pk_row = a.part + ((((int64_t)sp * a.B + b) * a.Hkv + hk) * a.Nk + my_key) * D;
@@ -580,6 +596,16 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
       }
     return;
   }
+  // dk and dv leave through LDS (as the forward's output): every wave is past its last read of
+  // the rings after this barrier; each wave writes its 32 keys' rows of dk, then dv, into a
+  // private region and stores them by whole rows; keys past Nk are dropped by the buffer range
+  // check. (n_split is uniform: every wave of a workgroup takes the same branch.)
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  constexpr int OROWB = D * ES, CPR = OROWB / 16, RPI = 1024 / OROWB;
+  static_assert(4 * 2 * 32 * OROWB <= 6 * TILEB, "the output stage fits in the rings");
+  const uint32_t stage_k = lds_addr_of(smem) + wave * 2 * 32 * OROWB, stage_v = stage_k + 32 * OROWB;
   const uint32_t dk_rowb = (uint32_t)(a.dk_n * ES), dv_rowb = (uint32_t)(a.dv_n * ES);
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -589,10 +615,19 @@ __global__ void __launch_bounds__(256) fa_bwd_dkdv_kernel(BwdArgs a) {
       const uint32_t k1v = TR::pack(dk[db][4 * q4 + 2] * a.scale, dk[db][4 * q4 + 3] * a.scale);
       const uint32_t v0v = TR::pack(dv[db][4 * q4 + 0], dv[db][4 * q4 + 1]);
       const uint32_t v1v = TR::pack(dv[db][4 * q4 + 2], dv[db][4 * q4 + 3]);
-      const uint32_t col = (db * 32 + q4 * 8 + hl * 4) * ES;
-      __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)k0v, (int)k1v}, dk_r, (uint32_t)my_key * dk_rowb + col, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b64(i32x2{(int)v0v, (int)v1v}, dv_r, (uint32_t)my_key * dv_rowb + col, 0, 0);
+      const uint32_t off = l32 * OROWB + (((db * 4 + q4) ^ (l32 % CPR)) << 4) + hl * 8;
+      lds_write_b64(stage_k + off, i32x2{(int)k0v, (int)k1v});
+      lds_write_b64(stage_v + off, i32x2{(int)v0v, (int)v1v});
     }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);   // the reads below follow the writes (one wave: in order)
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / CPR, c = lane % CPR;
+    const uint32_t so = r * OROWB + ((c ^ (r % CPR)) << 4);
+    const i32x4 kv = lds_read_b128(stage_k + so), vv = lds_read_b128(stage_v + so);
+    __builtin_amdgcn_raw_buffer_store_b128(kv, dk_r, (uint32_t)(kw0 + r) * dk_rowb + c * 16, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(vv, dv_r, (uint32_t)(kw0 + r) * dv_rowb + c * 16, 0, 0);
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
