@@ -16,7 +16,8 @@
 #include "fa_mask.hpp"
 
 namespace fa {
-hipError_t launch_fwd_f16(const FwdArgs& a, int D, int dtype, int block_n, int qb, int64_t grid, hipStream_t stream);
+hipError_t launch_fwd_f16(const FwdArgs& a, int D, int dtype, int block_n, int qb, int hp, int64_t grid,
+                          hipStream_t stream);
 hipError_t launch_fwd_fp8(const FwdArgs& a, int D, int64_t grid, hipStream_t stream);
 
 bool short_rows(int D, int dtype, int causal, int wl, int wr, bool sparse) {
@@ -25,7 +26,7 @@ bool short_rows(int D, int dtype, int causal, int wl, int wr, bool sparse) {
   return right >= 0 && (int64_t)wl + right + 1 <= kShortRowKeys;
 }
 
-TileShape tile_shape(int D, int dtype, bool few_keys, bool sparse) {
+TileShape tile_shape(int D, int dtype, bool few_keys, bool sparse, int group) {
   TileShape t;
   // fp16/bf16 at D = 128: 8 waves (two per SIMD, the register budget allows no more) and 64-key
   // tiles, one workgroup per compute unit. fp16/bf16 at D = 64: 4 waves of two 32-row query
@@ -39,7 +40,12 @@ TileShape tile_shape(int D, int dtype, bool few_keys, bool sparse) {
   const bool wide = f16 && D == 128 && !few_keys;
   t.waves = wide ? 8 : 4;
   t.qb = (f16 && D == 64 && !few_keys && !sparse) ? 2 : 1;
-  t.block_m = 32 * t.waves * t.qb;
+  // Few-keys calls with 4-way (or wider) GQA put 4 query heads of one K/V head in a workgroup,
+  // one wave each over the same 32 rows: each K/V tile brought into LDS serves all four, and the
+  // workgroup visits the 32 rows' key tiles only (a 128-row workgroup visits 3 more, which each
+  // of its waves skips or masks).
+  t.hp = (f16 && few_keys && !sparse && group % 4 == 0) ? 4 : 1;
+  t.block_m = 32 * t.waves * t.qb / t.hp;
   t.block_n = (f16 && (few_keys || t.qb == 2)) ? 32 : 64;
   const int es = dtype == FA_FP8_E4M3 ? 1 : 2;
   t.lds_bytes = (3 + 3) * t.block_n * D * es;   // three-slot K and V rings
@@ -48,7 +54,7 @@ TileShape tile_shape(int D, int dtype, bool few_keys, bool sparse) {
 
 hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, const TileShape& ts, int64_t grid, hipStream_t stream) {
   if (dtype == FA_FP8_E4M3) return launch_fwd_fp8(a, D, grid, stream);
-  return launch_fwd_f16(a, D, dtype, ts.block_n, ts.qb, grid, stream);
+  return launch_fwd_f16(a, D, dtype, ts.block_n, ts.qb, ts.hp, grid, stream);
 }
 }  // namespace fa
 
@@ -217,12 +223,13 @@ fa_status fa_fwd_plan(int B, int Nq, int Nk, int Hq, int Hkv, int D, int causal,
   const fa_status st = check_sizes(B, Nq, Nk, Hq, Hkv, D, window_left, window_right, dtype);
   if (st != FA_OK) return st;
   const fa::TileShape ts =
-      fa::tile_shape(D, dtype, fa::short_rows(D, dtype, causal, window_left, window_right, false), false);
+      fa::tile_shape(D, dtype, fa::short_rows(D, dtype, causal, window_left, window_right, false), false, Hq / Hkv);
   info->block_m = ts.block_m;
   info->block_n = ts.block_n;
   info->waves = ts.waves;
+  info->heads_per_wg = ts.hp;
   info->num_q_tiles = (Nq + ts.block_m - 1) / ts.block_m;
-  info->grid = (int64_t)B * Hq * info->num_q_tiles;
+  info->grid = (int64_t)B * (Hq / ts.hp) * info->num_q_tiles;
   info->lds_bytes = ts.lds_bytes;
   const fa::MaskSpec ms{Nq, Nk, causal ? 1 : 0, window_left, window_right};
   int64_t tiles = 0;
@@ -232,7 +239,7 @@ fa_status fa_fwd_plan(int B, int Nq, int Nk, int Hq, int Hkv, int D, int causal,
     fa::tile_range(ms, r0, r1, ts.block_n, &tb, &te);
     tiles += te - tb;
   }
-  info->kv_tiles = tiles * B * Hq;
+  info->kv_tiles = tiles * B * (Hq / ts.hp);
   return FA_OK;
 }
 
@@ -302,10 +309,10 @@ fa_status fwd_impl(const void* q, const void* k, const void* v, void* out, float
   a.nkb = (Nk + fa::kSparseBlockK - 1) / fa::kSparseBlockK;
   const bool sparse = block_mask != nullptr;
   const fa::TileShape ts =
-      fa::tile_shape(D, dtype, fa::short_rows(D, dtype, causal, window_left, window_right, sparse), sparse);
+      fa::tile_shape(D, dtype, fa::short_rows(D, dtype, causal, window_left, window_right, sparse), sparse, a.group);
   a.num_q_tiles = (Nq + ts.block_m - 1) / ts.block_m;
-  const int64_t grid = (int64_t)B * Hq * a.num_q_tiles;
-  a.sched = fa::make_schedule((int)grid, a.num_q_tiles, Hq, a.group, causal != 0, false);
+  const int64_t grid = (int64_t)B * (Hq / ts.hp) * a.num_q_tiles;
+  a.sched = fa::make_schedule((int)grid, a.num_q_tiles, Hq / ts.hp, a.group / ts.hp, causal != 0, false);
   const hipError_t e = fa::launch_fwd(a, D, dtype, ts, grid, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -397,10 +404,10 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* out, 
   a.total_q = total_q;
   a.total_k = total_k;
   const fa::TileShape ts =
-      fa::tile_shape(D, dtype, fa::short_rows(D, dtype, causal, window_left, window_right, false), false);
+      fa::tile_shape(D, dtype, fa::short_rows(D, dtype, causal, window_left, window_right, false), false, a.group);
   a.num_q_tiles = (max_seqlen_q + ts.block_m - 1) / ts.block_m;
-  const int64_t grid = (int64_t)B * Hq * a.num_q_tiles;
-  a.sched = fa::make_schedule((int)grid, a.num_q_tiles, Hq, a.group, causal != 0, true);
+  const int64_t grid = (int64_t)B * (Hq / ts.hp) * a.num_q_tiles;
+  a.sched = fa::make_schedule((int)grid, a.num_q_tiles, Hq / ts.hp, a.group / ts.hp, causal != 0, true);
   const hipError_t e = fa::launch_fwd(a, D, dtype, ts, grid, stream);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

@@ -44,11 +44,12 @@
 
 namespace fa {
 
-template <class TR, int D, int BN, int WAVES, int QB, bool SP>
+template <class TR, int D, int BN, int WAVES, int QB, bool SP, int HP>
 __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   constexpr int NT = WAVES * 64;        // threads per workgroup
   constexpr int WR = 32 * QB;           // query rows per wave: QB blocks of 32
-  constexpr int BM = WAVES * WR;        // query rows per workgroup
+  constexpr int WPH = WAVES / HP;       // waves per query head: HP heads sharing a K/V head
+  constexpr int BM = WPH * WR;          // query rows per workgroup (of each of its HP heads)
   constexpr int ES = 2;                 // bytes per stored element
   constexpr int ROWB = D * ES;          // bytes per K/V row in LDS
   constexpr int TILEB = BN * ROWB;      // bytes per K (or V) tile
@@ -60,6 +61,7 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   static_assert(BN * CPR % NT == 0, "tile must split evenly over the workgroup");
   static_assert(ROWB == 128 || ROWB == 256, "swizzles are laid out for 128- or 256-byte rows");
   static_assert(!SP || QB == 1, "block-sparse launches keep one query block per wave");
+  static_assert(WAVES % HP == 0 && (!SP || HP == 1), "whole waves per head; block-sparse keeps one head");
 
   constexpr int NS = 3;                 // ring slots per tensor
   __shared__ __attribute__((aligned(16))) char smem[2 * NS * TILEB];  // [K slots | V slots]
@@ -72,10 +74,13 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   const int hl = lane >> 5;      // half of the wave: which 16 of a block's 32 keys / k-slots
   const int l32 = lane & 31;     // query column of this lane inside each 32-row block of the wave
 
-  // ---- which (batch, head, query tile) this workgroup computes
-  int b, h, qt;
-  schedule_block(blockIdx.x, a.sched, &b, &h, &qt);
-  const int hk = (int)fdiv((uint32_t)h, a.sched.group);   // MQA/GQA: K/V head of this query head
+  // ---- which (batch, head, query tile) this workgroup computes. With HP > 1 the launch order
+  // counts groups of HP consecutive query heads (they share a K/V head: HP divides the GQA group),
+  // and wave w serves head HP * group + w / WPH: every K/V tile brought into LDS serves HP heads.
+  int b, hs, qt;
+  schedule_block(blockIdx.x, a.sched, &b, &hs, &qt);
+  const int h = hs * HP + wave / WPH;
+  const int hk = (int)fdiv((uint32_t)hs, a.sched.group);   // MQA/GQA: K/V head of this query head
   const int q0 = qt * BM;
   const SeqView sv = seq_view(a, b, h, D, ES, ES);
   if (q0 >= sv.Nq) return;                       // past the end of a shorter packed sequence
@@ -95,7 +100,7 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   const int wg_last = min(q0 + BM, sv.Nq) - 1;
   int tb, te;
   tile_range(ms, q0, wg_last, BN, &tb, &te);
-  const int w0 = q0 + wave * WR;
+  const int w0 = q0 + (wave % WPH) * WR;
   const bool wave_live = w0 < sv.Nq;
   const int w1 = min(w0 + WR - 1, sv.Nq - 1);
   int my_row[QB];   // this lane's query row in each block
@@ -111,7 +116,7 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
   if constexpr (SP) {
     const int mr0 = q0 / kSparseBlockQ;
     const int nrows = min(BM / kSparseBlockQ, a.nqb - mr0);
-    sp_row = (q0 + wave * WR) / kSparseBlockQ - mr0;
+    sp_row = w0 / kSparseBlockQ - mr0;
     const uint8_t* mrow = a.block_mask + ((int64_t)(a.mask_heads == 1 ? 0 : h) * a.nqb + mr0) * a.nkb;
     if (wave == 0) {
       int cnt = 0;
@@ -524,29 +529,34 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_kernel(FwdArgs a) {
 }
 
 template <class TR, int D>
-static hipError_t launch_t(const FwdArgs& a, int block_n, int qb, int64_t grid, hipStream_t stream) {
+static hipError_t launch_t(const FwdArgs& a, int block_n, int qb, int hp, int64_t grid, hipStream_t stream) {
   constexpr int BN = 64, WAVES = D == 64 ? 4 : 8;
   static_assert(BN == kSparseBlockK && (WAVES * 32) % kSparseBlockQ == 0, "tiles nest in the mask's blocks");
   if (a.block_mask != nullptr)
-    hipLaunchKernelGGL((fa_fwd_kernel<TR, D, BN, WAVES, 1, true>), dim3((unsigned)grid), dim3(WAVES * 64),
+    hipLaunchKernelGGL((fa_fwd_kernel<TR, D, BN, WAVES, 1, true, 1>), dim3((unsigned)grid), dim3(WAVES * 64),
                        (size_t)(2 * a.nkb + 1) * 4, stream, a);
   else if (qb == 2) {   // D = 64: two query blocks per wave, 32-key tiles
     if constexpr (D == 64)
-      hipLaunchKernelGGL((fa_fwd_kernel<TR, D, 32, 4, 2, false>), dim3((unsigned)grid), dim3(4 * 64), 0, stream, a);
+      hipLaunchKernelGGL((fa_fwd_kernel<TR, D, 32, 4, 2, false, 1>), dim3((unsigned)grid), dim3(4 * 64), 0, stream, a);
     else
       return hipErrorInvalidValue;
-  } else if (block_n == 32)   // rows with few keys: 4 waves, 32-key tiles
-    hipLaunchKernelGGL((fa_fwd_kernel<TR, D, 32, 4, 1, false>), dim3((unsigned)grid), dim3(4 * 64), 0, stream, a);
+  } else if (block_n == 32 && hp == 4)   // rows with few keys, 4 query heads of one K/V head
+    hipLaunchKernelGGL((fa_fwd_kernel<TR, D, 32, 4, 1, false, 4>), dim3((unsigned)grid), dim3(4 * 64), 0, stream, a);
+  else if (block_n == 32)   // rows with few keys: 4 waves, 32-key tiles
+    hipLaunchKernelGGL((fa_fwd_kernel<TR, D, 32, 4, 1, false, 1>), dim3((unsigned)grid), dim3(4 * 64), 0, stream, a);
   else
-    hipLaunchKernelGGL((fa_fwd_kernel<TR, D, BN, WAVES, 1, false>), dim3((unsigned)grid), dim3(WAVES * 64), 0, stream,
-                       a);
+    hipLaunchKernelGGL((fa_fwd_kernel<TR, D, BN, WAVES, 1, false, 1>), dim3((unsigned)grid), dim3(WAVES * 64), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_f16(const FwdArgs& a, int D, int dtype, int block_n, int qb, int64_t grid, hipStream_t stream) {
+hipError_t launch_fwd_f16(const FwdArgs& a, int D, int dtype, int block_n, int qb, int hp, int64_t grid,
+                          hipStream_t stream) {
   if (dtype == 0)
-    return D == 64 ? launch_t<F16, 64>(a, block_n, qb, grid, stream) : launch_t<F16, 128>(a, block_n, qb, grid, stream);
-  return D == 64 ? launch_t<BF16, 64>(a, block_n, qb, grid, stream) : launch_t<BF16, 128>(a, block_n, qb, grid, stream);
+    return D == 64 ? launch_t<F16, 64>(a, block_n, qb, hp, grid, stream)
+                   : launch_t<F16, 128>(a, block_n, qb, hp, grid, stream);
+  return D == 64 ? launch_t<BF16, 64>(a, block_n, qb, hp, grid, stream)
+                 : launch_t<BF16, 128>(a, block_n, qb, hp, grid, stream);
 }
 
 }  // namespace fa

@@ -142,6 +142,7 @@ hipError_t launch_bwd(const BwdArgs& a, int D, int dtype, hipStream_t stream);
 // Tile shapes of the launch for head dimension D and storage type.
 struct TileShape {
   int block_m, block_n, waves, qb, lds_bytes;   // qb: query blocks of 32 rows per wave
+  int hp;   // query heads per workgroup (they share a K/V head); block_m rows of each
 };
 
 // Whether a fp16/bf16 call takes the few-keys launch shape (4-wave workgroups, 32-key tiles):
@@ -149,7 +150,7 @@ struct TileShape {
 // block-sparse.
 constexpr int kShortRowKeys = 4096;
 bool short_rows(int D, int dtype, int causal, int wl, int wr, bool sparse);
-TileShape tile_shape(int D, int dtype, bool few_keys, bool sparse);
+TileShape tile_shape(int D, int dtype, bool few_keys, bool sparse, int group);
 hipError_t launch_fwd(const FwdArgs& a, int D, int dtype, const TileShape& ts, int64_t grid, hipStream_t stream);
 
 }  // namespace fa

@@ -43,7 +43,7 @@ class FaVarlenStrides(ctypes.Structure):
 class FaPlanInfo(ctypes.Structure):
     _fields_ = [("block_m", ctypes.c_int), ("block_n", ctypes.c_int), ("waves", ctypes.c_int),
                 ("num_q_tiles", ctypes.c_int), ("grid", ctypes.c_int64), ("lds_bytes", ctypes.c_int),
-                ("kv_tiles", ctypes.c_int64)]
+                ("kv_tiles", ctypes.c_int64), ("heads_per_wg", ctypes.c_int)]
 
 
 class FaError(RuntimeError):

@@ -281,13 +281,14 @@ const char* fa_status_str(fa_status s);
 
 /* Launch plan of one fa_fwd call (host only, no device call). */
 typedef struct fa_plan_info {
-  int block_m;        /* query rows per workgroup                                   */
+  int block_m;        /* query rows per workgroup, of each of its heads             */
   int block_n;        /* keys per K/V tile                                          */
   int waves;          /* wavefronts per workgroup                                   */
   int num_q_tiles;    /* ceil(Nq / block_m)                                         */
-  int64_t grid;       /* workgroups launched = B * Hq * num_q_tiles                 */
+  int64_t grid;       /* workgroups launched = B * (Hq / heads_per_wg) * num_q_tiles */
   int lds_bytes;      /* LDS per workgroup                                          */
   int64_t kv_tiles;   /* K/V tiles visited, summed over all workgroups              */
+  int heads_per_wg;   /* query heads per workgroup (sharing a K/V head), block_m rows each */
 } fa_plan_info;
 
 /*

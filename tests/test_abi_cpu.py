@@ -216,6 +216,22 @@ def _window_key_tiles(Nq, Nk, causal, window, block_m, block_n):
     return total
 
 
+@pytest.mark.parametrize("Hq,Hkv,hp", [(32, 8, 4), (32, 1, 4), (8, 2, 4), (12, 3, 4), (24, 2, 4), (6, 3, 1), (4, 2, 1), (4, 4, 1)])
+@pytest.mark.parametrize("D", [64, 128])
+def test_plan_few_keys_packs_gqa_heads(lib, Hq, Hkv, hp, D):
+    # few-keys calls whose query heads share a K/V head 4 (or more, a multiple of 4) ways put 4
+    # such heads in a workgroup, one wave each over the same 32 rows; other groups keep one head
+    Nq, Nk, window = 1000, 1100, (256, 256)
+    p = fa.plan(2, Nq, Nk, Hq, Hkv, D, causal=True, window=window, dtype=fa.FA_BF16)
+    bm = 128 // hp
+    assert (p["block_m"], p["block_n"], p["waves"], p["heads_per_wg"]) == (bm, 32, 4, hp)
+    assert p["num_q_tiles"] == -(-Nq // bm) and p["grid"] == 2 * (Hq // hp) * p["num_q_tiles"]
+    assert p["kv_tiles"] == 2 * (Hq // hp) * _window_key_tiles(Nq, Nk, True, window, bm, 32)
+    # full causal rows do not take the few-keys shape: one head per workgroup
+    q = fa.plan(2, Nq, Nk, Hq, Hkv, D, causal=True, dtype=fa.FA_BF16)
+    assert q["heads_per_wg"] == 1
+
+
 @pytest.mark.parametrize("causal,window,few", [(False, (100, 30), True), (True, (256, 256), True),
                                                (True, (4095, -1), True), (True, (4096, -1), False),
                                                (False, (1000, 100), True), (False, (4000, 100), False),

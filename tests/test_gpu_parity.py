@@ -60,6 +60,11 @@ RAGGED = [
     (2, 150, 333, 4, 2, 64, False, (50, 20)),
     (1, 1000, 700, 2, 1, 128, True, (200, -1)),
     (1, 97, 4100, 2, 2, 128, False, (4000, 95)),
+    # few-keys calls with 4-way (or wider) GQA: four query heads of one K/V head per workgroup
+    (2, 150, 333, 8, 2, 64, False, (50, 20)),
+    (1, 1000, 700, 8, 1, 128, True, (200, -1)),
+    (1, 97, 4100, 8, 2, 128, False, (4000, 95)),
+    (3, 190, 190, 12, 3, 64, True, (64, -1)),       # group 4, heads not a multiple of 8
 ]
 
 
@@ -78,6 +83,8 @@ NAN_TAIL = [
     (1, 150, 290, 4, 1, 128, True, (-1, -1), "bf16"),
     (2, 150, 333, 4, 2, 64, False, (50, 20), "bf16"),      # few-keys launch shape (32-key tiles)
     (1, 300, 301, 2, 2, 128, True, (100, -1), "f16"),      # few-keys launch shape
+    (1, 300, 301, 8, 2, 128, True, (100, -1), "bf16"),     # few-keys shape, four heads per workgroup
+    (2, 150, 333, 8, 1, 64, False, (50, 20), "f16"),
     (1, 200, 300, 4, 1, 128, False, (-1, -1), "e4m3"),
     (2, 333, 333, 4, 2, 64, True, (-1, -1), "e4m3"),
 ]

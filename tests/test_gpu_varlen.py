@@ -47,6 +47,9 @@ MIXES = [
     # 8 K/V heads per sequence: the launch deals K/V heads over the XCDs by chunks of query heads
     ([300, 1000, 77, 512], None, 16, 8, 64, True, (-1, -1)),
     ([129, 640], None, 8, 8, 128, False, (-1, -1)),
+    # windows with 4-way GQA: four query heads of one K/V head per workgroup
+    ([300, 1000, 77, 512], None, 16, 4, 128, True, (100, -1)),
+    ([200, 0, 333], [250, 40, 333], 8, 2, 64, False, (60, 30)),
 ]
 
 
