@@ -44,7 +44,7 @@ TileShape tile_shape(int D, int dtype, bool few_keys, bool sparse, int group) {
   // one wave each over the same 32 rows: each K/V tile brought into LDS serves all four, and the
   // workgroup visits the 32 rows' key tiles only (a 128-row workgroup visits 3 more, which each
   // of its waves skips or masks).
-  t.hp = (f16 && few_keys && !sparse && group % 4 == 0) ? 4 : 1;
+  t.hp = (f16 && (few_keys || wide) && !sparse && group % 4 == 0) ? 4 : 1;
   t.block_m = 32 * t.waves * t.qb / t.hp;
   t.block_n = (f16 && (few_keys || t.qb == 2)) ? 32 : 64;
   const int es = dtype == FA_FP8_E4M3 ? 1 : 2;

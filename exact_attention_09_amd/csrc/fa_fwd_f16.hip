@@ -544,6 +544,9 @@ static hipError_t launch_t(const FwdArgs& a, int block_n, int qb, int hp, int64_
     hipLaunchKernelGGL((fa_fwd_kernel<TR, D, 32, 4, 1, false, 4>), dim3((unsigned)grid), dim3(4 * 64), 0, stream, a);
   else if (block_n == 32)   // rows with few keys: 4 waves, 32-key tiles
     hipLaunchKernelGGL((fa_fwd_kernel<TR, D, 32, 4, 1, false, 1>), dim3((unsigned)grid), dim3(4 * 64), 0, stream, a);
+  else if (hp == 4 && WAVES == 8)   // D = 128 with 4-way GQA: 4 heads x 64 rows
+    hipLaunchKernelGGL((fa_fwd_kernel<TR, D, BN, WAVES, 1, false, 4>), dim3((unsigned)grid), dim3(WAVES * 64), 0,
+                       stream, a);
   else
     hipLaunchKernelGGL((fa_fwd_kernel<TR, D, BN, WAVES, 1, false, 1>), dim3((unsigned)grid), dim3(WAVES * 64), 0,
                        stream, a);

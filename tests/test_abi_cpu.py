@@ -187,9 +187,12 @@ def test_plan(lib):
     assert p["grid"] == 4 * 32 * 16
     assert p["kv_tiles"] == 4 * 32 * sum(8 * (t + 1) for t in range(16))
     assert p["lds_bytes"] == 6 * 32 * 64 * 2
-    # D = 128 runs 8 waves (256 rows per workgroup)
+    # D = 128 runs 8 waves: 256 rows of one head, or with 4-way GQA 64 rows of 4 heads
+    p = fa.plan(1, 16384, 16384, 32, 32, 128, causal=True, dtype=fa.FA_BF16)
+    assert p["block_m"] == 256 and p["waves"] == 8 and p["num_q_tiles"] == 64 and p["heads_per_wg"] == 1
     p = fa.plan(1, 16384, 16384, 32, 8, 128, causal=True, dtype=fa.FA_BF16)
-    assert p["block_m"] == 256 and p["waves"] == 8 and p["num_q_tiles"] == 64
+    assert p["block_m"] == 64 and p["waves"] == 8 and p["num_q_tiles"] == 256 and p["heads_per_wg"] == 4
+    assert p["grid"] == 8 * 256
     # fp8: 4-wave kernel
     p = fa.plan(2, 4096, 4096, 32, 32, 64, causal=True, dtype=fa.FA_FP8_E4M3)
     assert p["block_m"] == 128 and p["grid"] == 2 * 32 * 32
@@ -227,9 +230,11 @@ def test_plan_few_keys_packs_gqa_heads(lib, Hq, Hkv, hp, D):
     assert (p["block_m"], p["block_n"], p["waves"], p["heads_per_wg"]) == (bm, 32, 4, hp)
     assert p["num_q_tiles"] == -(-Nq // bm) and p["grid"] == 2 * (Hq // hp) * p["num_q_tiles"]
     assert p["kv_tiles"] == 2 * (Hq // hp) * _window_key_tiles(Nq, Nk, True, window, bm, 32)
-    # full causal rows do not take the few-keys shape: one head per workgroup
+    # full causal rows: at D = 128 the 8-wave shape packs the same way (64 rows of 4 heads), at
+    # D = 64 the two-block shape keeps one head
     q = fa.plan(2, Nq, Nk, Hq, Hkv, D, causal=True, dtype=fa.FA_BF16)
-    assert q["heads_per_wg"] == 1
+    assert q["heads_per_wg"] == (hp if D == 128 else 1)
+    assert q["block_m"] == (256 // q["heads_per_wg"] if D == 128 else 256)
 
 
 @pytest.mark.parametrize("causal,window,few", [(False, (100, 30), True), (True, (256, 256), True),

@@ -65,6 +65,9 @@ RAGGED = [
     (1, 1000, 700, 8, 1, 128, True, (200, -1)),
     (1, 97, 4100, 8, 2, 128, False, (4000, 95)),
     (3, 190, 190, 12, 3, 64, True, (64, -1)),       # group 4, heads not a multiple of 8
+    # D = 128 with 4-way GQA, full rows: the 8-wave shape with four heads of 64 rows
+    (1, 333, 300, 8, 2, 128, True, (-1, -1)),
+    (2, 129, 257, 12, 3, 128, False, (-1, -1)),
 ]
 
 
@@ -85,6 +88,7 @@ NAN_TAIL = [
     (1, 300, 301, 2, 2, 128, True, (100, -1), "f16"),      # few-keys launch shape
     (1, 300, 301, 8, 2, 128, True, (100, -1), "bf16"),     # few-keys shape, four heads per workgroup
     (2, 150, 333, 8, 1, 64, False, (50, 20), "f16"),
+    (1, 150, 290, 8, 2, 128, True, (-1, -1), "bf16"),      # 8-wave shape, four heads per workgroup
     (1, 200, 300, 4, 1, 128, False, (-1, -1), "e4m3"),
     (2, 333, 333, 4, 2, 64, True, (-1, -1), "e4m3"),
 ]
