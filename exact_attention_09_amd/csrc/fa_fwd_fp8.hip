@@ -12,10 +12,13 @@
 //    holds 32 consecutive k-slots, so one MFMA covers 64 head-dim values of S^T = K Q^T, and one
 //    covers 64 keys of O^T = V^T P^T.
 //  * P is rounded to e4m3 after a 2^8 shift that keeps small weights above the format's
-//    subnormal range. To keep p * 2^8 <= 448 (the largest e4m3 value), the row reference m moves
-//    whenever a tile's row max exceeds it by more than 0.8 (log2 units): p <= 2^0.8; a move puts
-//    m 2 above the tile's max, so moves (and their rescaling of O) are rare. The running sum
-//    (and so the lse) uses the unrounded fp32 p.
+//    subnormal range. p * 2^8 must stay <= 448 (the largest e4m3 value). The exponentials of a
+//    tile are taken against the reference m of the tiles before it, without the tile's row max;
+//    only when a lane's sum of 2^8 p exceeds 448 (the one case in which a single term can) does
+//    the wave take the row max, and m moves if that max exceeds it by more than 0.8 (log2 units),
+//    to 4 above the max, with O and l rescaled and the tile's exponentials taken again. With the
+//    row max at weight 2^(8 - 4) = 16, a lane's 32 keys rarely sum past 448. The running sum (and
+//    so the lse) uses the unrounded fp32 p.
 //  * V^T is read with ds_read_b64_tr_b8: a lane receives 8 consecutive LDS rows of one column.
 //    The 16 keys a lane half holds in the S^T accumulator (keys g*8 + half*4 + e, g, e < 4, of
 //    each 32-key block) are stored as 16 consecutive LDS rows (row half*16 + g*4 + e): the HBM ->
@@ -36,10 +39,13 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // after the move and the next move needs a rise of kTau8 + kLift: fewer moves (each rescales O).
 // kLift is a whole number, so the weight of the max itself, 2^(8 - kLift) after the shift, is an
 // exact e4m3 value (as 2^8 was without the lift); weights down to 2^(-14 + kLift) of the row max
-// stay in e4m3's normal range.
+// stay in e4m3's normal range. A lane's sum of 2^8 p at most kSumBound8 = 448 bounds each term.
+// (A lift of 2 would make that sum exceed 448 in about a quarter of the tiles of a random causal
+// [4096, 64] head, 4 in about 3%, the share in which the reference is set or moves anyway.)
 constexpr float kPShiftLog2 = 8.0f;
 constexpr float kTau8 = 0.8f;
-constexpr float kLift = 2.0f;
+constexpr float kLift = 4.0f;
+constexpr float kSumBound8 = 448.0f;
 
 // 64-bank LDS swizzles (16-byte chunk XOR) for 64- and 128-byte rows.
 template <int ROWB>
@@ -219,11 +225,9 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_fp8_kernel(FwdArgs a) {
   };
 
   // ---- software pipeline, as in the 16-bit kernel: step j issues the loads of K(j+3) and V(j+1),
-  // runs PV(j-1) and S(j+1) on the matrix pipe and the softmax of tile j on the vector pipe.
-  // The softmax needs the tile's row max before its exponentials (the reference may have to
-  // move), so a step has two interleaved halves: PV(j-1) with the row max, then, after the
-  // reference update (which rescales O, already holding PV(j-1)), S(j+1) with the
-  // exponentials. r0, r1, r2: byte offsets of ring slots (j - tb) % 3, +1, +2.
+  // runs PV(j-1) and S(j+1) on the matrix pipe and the softmax of tile j on the vector pipe
+  // (against the reference of the tiles before it, checked afterwards by the lanes' sums).
+  // r0, r1, r2: byte offsets of ring slots (j - tb) % 3, +1, +2.
   const int need_lo = jlo - 1;
   const uint32_t need_n = jlo < jhi ? (uint32_t)(jhi - jlo + 2) : 0u;
   const uint32_t full_n = fhi > flo ? (uint32_t)(fhi - flo) : 0u;
@@ -275,63 +279,68 @@ __global__ void __launch_bounds__(WAVES * 64) fa_fwd_fp8_kernel(FwdArgs a) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) sn[kb] = f32x16{};
       const i32x8 pop = i32x8{pp[0], pp[1], pp[2], pp[3], pp[4], pp[5], pp[6], pp[7]};
-      // first half: PV(j-1) and the row max. Each PV MFMA follows a share of the max (which
-      // needs no LDS operand), so the V reads issued above have that long to land; each MFMA
-      // waits only for its own operand. Two max chains give the vector pipe independent work.
+      // 2^8 p = exp2(s c - m + 8) for the tile's code words wq (kb = wq / 4, w4 = wq % 4), against
+      // the reference of the tiles before it; rs sums this lane's unrounded values (from -0, which
+      // the first addition leaves out). The two conversions of a word write its low and high
+      // halves, so the word's old value (codes of tile j - 2, read by the step before) is a free
+      // first operand.
+      float rs = -0.f;
+      auto codes = [&](int wq, float shift) {
+        const int kb = wq / 4, w4 = wq % 4;
+        float p[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][4 * w4 + u], c2, shift));
+          rs += p[u];
+        }
+        const int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pc[wq], false);
+        pc[wq] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
+        asm volatile("" ::"v"(pc[wq]), "v"(rs));
+      };
+      const float shift = kPShiftLog2 - m;
+      // PV(j-1) with the first four code words, then S(j+1) with the last four. The V and K
+      // operands were read above; each MFMA waits only for its own.
+      constexpr int WPV = 4 / DB, WS = 4 / NSM;   // code words per PV and per S MFMA
+      static_assert(WPV * DB == 4 && WS * NSM == 4, "the code words split evenly over the MFMAs");
       __builtin_amdgcn_s_setprio(1);
       __builtin_amdgcn_sched_barrier(0);
-      float mx0 = sc[0][0], mx1 = sc[0][1];
-      constexpr int MAXPER = KB * 16 / DB;   // max-ed values per PV MFMA
-      static_assert(MAXPER % 4 == 0, "two chains of three-input maxima");
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-#pragma unroll
-        for (int q = db * MAXPER; q < (db + 1) * MAXPER; q += 4) {
-          mx0 = max3(mx0, sc[q / 16][q % 16], sc[q / 16][q % 16 + 1]);
-          mx1 = max3(mx1, sc[q / 16][q % 16 + 2], sc[q / 16][q % 16 + 3]);
-        }
-        asm volatile("" ::"v"(mx0), "v"(mx1));
-        __builtin_amdgcn_sched_barrier(0);
         o[db] = mfma_fp8(vop[db], pop, o[db]);
+#pragma unroll
+        for (int wq = db * WPV; wq < (db + 1) * WPV; ++wq) codes(wq, shift);
         __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_s_setprio(0);
-      // reference update (lazy: p <= 2^0.8 keeps 2^8 p inside the e4m3 range). A move places the
-      // reference kLift above the tile's max, so the next move needs a rise of kTau8 + kLift.
-      const float mx = pair_max(fmaxf(mx0, mx1)) * c2;
-      const float m_new = mx > m + kTau8 ? mx + kLift : m;
-      if (__builtin_amdgcn_ballot_w64(m_new != m)) {
-        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[db] *= alpha;
-      }
-      m = m_new;
-      // second half: S(j+1) and 2^8 p = exp2(s c - m + 8), its fp32 sum and its e4m3 codes
-      const float shift = kPShiftLog2 - m;
-      float rs = 0.f;
-      __builtin_amdgcn_s_setprio(1);
-      __builtin_amdgcn_sched_barrier(0);
-      constexpr int WPER = 8 / NSM;          // code words per S MFMA
 #pragma unroll
       for (int e = 0; e < NSM; ++e) {
         sn[e % KB] = mfma_fp8(kop[e], qop[e / KB], sn[e % KB]);
 #pragma unroll
-        for (int wq = e * WPER; wq < (e + 1) * WPER; ++wq) {
-          const int kb = wq / 4, w4 = wq % 4;
-          float p[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][4 * w4 + u], c2, shift));
-            rs += p[u];
-          }
-          const int w = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-          pc[wq] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], w, true);
-          asm volatile("" ::"v"(pc[wq]), "v"(rs));
-        }
+        for (int wq = 4 + e * WS; wq < 4 + (e + 1) * WS; ++wq) codes(wq, shift);
         __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_s_setprio(0);
+      // a term can exceed 448 only if its lane's sum does (the first tile with an admitted key
+      // always does: m starts at -1e30). Then the row max decides whether m moves; O already
+      // holds PV(j-1), whose codes were taken against the old m, and is rescaled with l.
+      if (__builtin_amdgcn_ballot_w64(!(rs <= kSumBound8))) {
+        float mx = sc[0][0];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+        const float mxc = pair_max(mx) * c2;
+        const float m_new = mxc > m + kTau8 ? mxc + kLift : m;
+        if (__builtin_amdgcn_ballot_w64(m_new != m)) {
+          const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+          l *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) o[db] *= alpha;
+          m = m_new;
+          rs = -0.f;
+#pragma unroll
+          for (int wq = 0; wq < 8; ++wq) codes(wq, kPShiftLog2 - m);
+        }
+      }
       l += rs;
     }
     barrier_keep(CH * ((int)k3 + (int)v1));
