@@ -360,3 +360,32 @@ def test_fp8_mask_probe_exact(case):
             assert np.array_equal(got_cnt, cnt)
             o = out[0, :, h, :].float().numpy().astype(np.float64)
             assert np.array_equal(np.rint(o * cnt[:, None]).astype(np.int64), per)
+
+
+def _fp8_reference_inputs(kind, N, H, D):
+    """Scores built to drive the fp8 kernel's reference logic (1 batch, H heads, fp8 codes)."""
+    g = torch.Generator().manual_seed(77)
+    v = torch.randn(1, N, H, D, generator=g)
+    if kind == "rising":      # every row's max climbs along the keys: the reference moves tile after tile
+        q = torch.ones(1, N, H, D)
+        k = torch.linspace(0.0, 2.0, N).view(1, N, 1, 1).expand(1, N, H, D).clone()
+    elif kind == "flat":      # all scores equal: each lane's 32 terms sum past 448 with no rise of the max
+        q = torch.zeros(1, N, H, D)
+        k = torch.randn(1, N, H, D, generator=g)
+    else:                     # "jump": random scores, then one key far above all others late in the row
+        q = torch.randn(1, N, H, D, generator=g).abs()
+        k = torch.randn(1, N, H, D, generator=g)
+        k[0, N - 100] = 3.0
+    f8 = torch.float8_e4m3fn
+    return q.to(f8), k.to(f8), v.to(f8)
+
+
+@pytest.mark.parametrize("kind,causal", [("rising", True), ("rising", False), ("flat", False), ("flat", True),
+                                         ("jump", False)])
+def test_fp8_reference_moves(kind, causal):
+    """The fp8 kernel takes its exponentials against the previous tiles' reference and checks each
+    lane's sum against 448 afterwards: rows whose max keeps rising (a move, a rescale and a second
+    pass in most tiles), rows with many equal weights (the check trips without a move) and a late
+    jump must all match the oracle."""
+    q, k, v = _fp8_reference_inputs(kind, 1000, 2, 64)
+    full_check(q, k, v, causal, (-1, -1), 0.125, descale=(1.0, 1.0, 1.0), what=f"fp8 {kind} causal={causal}")
