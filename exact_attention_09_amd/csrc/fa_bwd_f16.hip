@@ -9,12 +9,13 @@
 //     dq_i = scale sum_j ds_ij k_j             dk_j = scale sum_i ds_ij q_i
 // and a K/V head shared by several query heads (MQA/GQA) receives the sum of their terms.
 //
-// Three kernels, none with atomics (the result is deterministic):
-//  * delta: rowsum(dout * out) per query row, into a caller-provided fp32 workspace;
+// Two kernels, none with atomics (the result is deterministic), run in this order:
 //  * dq: one workgroup per (batch, query head, 128 query rows), walking the K/V tiles the rows
 //    attend to. Lanes own queries, as in the forward kernel: S^T = K Q^T and dP^T = V dO^T come
 //    out with one query per lane, so lse_i and delta_i are per-lane scalars, and dS^T is the B
-//    operand of dQ^T = K^T dS^T with K^T read by ds_read_b64_tr_b16 in the matching key order;
+//    operand of dQ^T = K^T dS^T with K^T read by ds_read_b64_tr_b16 in the matching key order.
+//    Each lane computes its row's delta from the dout values it holds and the same values of out,
+//    and writes -delta and -lse / scale into a caller-provided fp32 workspace;
 //  * dk/dv: one workgroup per (batch, K/V head, 128 keys), walking the query tiles (of every
 //    query head that reads this K/V head) that attend to its keys. Lanes own keys: S = Q K^T and
 //    dP = dO V^T come out with one key per lane; P and dS are the B operands of
@@ -51,42 +52,6 @@ __device__ inline void unpack2(uint32_t w, float& x, float& y) {
 constexpr float kLog2e = 1.44269504088896340736f;
 
 // ---------------------------------------------------------------------------------------------
-// Per query row r = (b, h, i), into the two halves of the workspace: -delta[r], with
-// delta[r] = sum_d dout[b, i, h, d] * out[b, i, h, d], and -lse[r] / softmax_scale, the row's
-// offset in units of raw scores (-inf for a row with no admitted key, so that its p is 0).
-// D/8 lanes per row, 16 bytes each.
-template <class TR, int D>
-__global__ void __launch_bounds__(256) fa_bwd_delta_kernel(BwdArgs a) {
-  constexpr int LPR = D / 8;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = gid / LPR;
-  const int part = (int)(gid % LPR);
-  const int64_t nrows = (int64_t)a.B * a.Hq * a.Nq;
-  float s = 0.f;
-  if (row < nrows) {
-    const int i = (int)(row % a.Nq);
-    const int64_t bh = row / a.Nq;
-    const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
-    const i32x4 o = *(const i32x4*)((const char*)a.o + (b * a.o_b + i * a.o_n + h * a.o_h + part * 8) * 2);
-    const i32x4 d = *(const i32x4*)((const char*)a.dout + (b * a.do_b + i * a.do_n + h * a.do_h + part * 8) * 2);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float o0, o1, d0, d1;
-      unpack2<TR>((uint32_t)o[e], o0, o1);
-      unpack2<TR>((uint32_t)d[e], d0, d1);
-      s = __builtin_fmaf(o0, d0, __builtin_fmaf(o1, d1, s));
-    }
-  }
-#pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-  if (row < nrows && part == 0) {
-    a.delta[row] = -s;
-    const float l = a.lse[row];
-    a.delta[nrows + row] = l > -INFINITY ? -l / a.scale : -INFINITY;
-  }
-}
-
-// ---------------------------------------------------------------------------------------------
 template <class TR, int D>
 __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(BwdArgs a) {
   using T = OpTile<D>;
@@ -110,6 +75,7 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(BwdArgs a) {
   const char* vbp = (const char*)a.v + (b * a.v_b + hk * a.v_h) * ES;
   const __amdgpu_buffer_rsrc_t q_r = make_rsrc((const char*)a.q + (b * a.q_b + h * a.q_h) * ES, a.q_bytes);
   const __amdgpu_buffer_rsrc_t do_r = make_rsrc((const char*)a.dout + (b * a.do_b + h * a.do_h) * ES, a.do_bytes);
+  const __amdgpu_buffer_rsrc_t o_r = make_rsrc((const char*)a.o + (b * a.o_b + h * a.o_h) * ES, a.o_bytes);
   const __amdgpu_buffer_rsrc_t dq_r = make_rsrc((char*)a.dq + (b * a.dq_b + h * a.dq_h) * ES, a.dq_bytes);
   const uint32_t k_rowb = (uint32_t)(a.k_n * ES), v_rowb = (uint32_t)(a.v_n * ES);
 
@@ -129,21 +95,39 @@ __global__ void __launch_bounds__(256) fa_bwd_dq_kernel(BwdArgs a) {
   const int hi_i = clamp_key(key_hi(ms, my_row));
   const uint32_t span_i = hi_i >= lo_i ? (uint32_t)(hi_i - lo_i + 1) : 0u;
 
-  // this lane's query row: Q and dO as B operands, lse (base 2) and delta
-  i32x4 qop[KS], dop[KS];
+  // this lane's query row: Q and dO as B operands (head-dim values ks*16 + hl*8 .. +7), and the
+  // same values of out for delta
+  i32x4 qop[KS], dop[KS], oop[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     qop[ks] = __builtin_amdgcn_raw_buffer_load_b128(q_r, (uint32_t)my_row * (uint32_t)(a.q_n * ES) + (ks * 16 + hl * 8) * ES, 0, 0);
     dop[ks] = __builtin_amdgcn_raw_buffer_load_b128(do_r, (uint32_t)my_row * (uint32_t)(a.do_n * ES) + (ks * 16 + hl * 8) * ES, 0, 0);
+    oop[ks] = __builtin_amdgcn_raw_buffer_load_b128(o_r, (uint32_t)my_row * (uint32_t)(a.o_n * ES) + (ks * 16 + hl * 8) * ES, 0, 0);
   }
-  float lse2 = INFINITY, ndelta = 0.f;   // rows past the end or with no key: p = 0
-  if (my_row < a.Nq) {
-    const int64_t r = ((int64_t)b * a.Hq + h) * a.Nq + my_row;
-    const float l = a.lse[r];
-    if (l > -INFINITY) lse2 = l * kLog2e;
-    ndelta = a.delta[r];                // -delta
-  }
+  const int64_t nrows = (int64_t)a.B * a.Hq * a.Nq;
+  const int64_t r = ((int64_t)b * a.Hq + h) * a.Nq + my_row;
+  const float l_row = my_row < a.Nq ? a.lse[r] : -INFINITY;
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+  // delta = rowsum(dout * out): this lane's half of the head dimension, then its partner's (lane
+  // l ^ 32 holds the other half of the row). It goes into the workspace with -lse / scale, for the
+  // dk/dv kernel, which runs after this one.
+  float dpart = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float o0, o1, d0, d1;
+      unpack2<TR>((uint32_t)oop[ks][e], o0, o1);
+      unpack2<TR>((uint32_t)dop[ks][e], d0, d1);
+      dpart = __builtin_fmaf(o0, d0, __builtin_fmaf(o1, d1, dpart));
+    }
+  const float ndelta = -(dpart + __shfl_xor(dpart, 32));   // -delta; rows past the end: 0
+  float lse2 = INFINITY;                // rows past the end or with no key: p = 0
+  if (l_row > -INFINITY) lse2 = l_row * kLog2e;
+  if (my_row < a.Nq && hl == 0) {
+    a.delta[r] = ndelta;
+    a.delta[nrows + r] = l_row > -INFINITY ? -l_row / a.scale : -INFINITY;
+  }
 
   uint32_t kgoff[CH], vgoff[CH];
 #pragma unroll
@@ -682,17 +666,15 @@ __global__ void __launch_bounds__(256) fa_bwd_reduce_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------------------------
 template <class TR, int D>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
-  const int64_t rows = (int64_t)a.B * a.Hq * a.Nq;
-  const int64_t delta_blocks = (rows * (D / 8) + 255) / 256;
-  hipLaunchKernelGGL((fa_bwd_delta_kernel<TR, D>), dim3((unsigned)delta_blocks), dim3(256), 0, stream, a);
+  // dq first: it also writes the workspace rows (-delta, -lse / scale) that dk/dv reads
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<TR, D>), dim3((unsigned)((int64_t)a.B * a.Hq * a.num_q_tiles)), dim3(256), 0,
+                     stream, a);
   hipLaunchKernelGGL((fa_bwd_dkdv_kernel<TR, D>),
                      dim3((unsigned)((int64_t)a.B * a.Hkv * a.n_split * a.num_k_tiles)), dim3(256), 0, stream, a);
   if (a.n_split > 1) {
     const int64_t quads = (int64_t)a.B * a.Hkv * a.Nk * (D / 4);
     hipLaunchKernelGGL((fa_bwd_reduce_kernel<TR, D>), dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, stream, a);
   }
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<TR, D>), dim3((unsigned)((int64_t)a.B * a.Hq * a.num_q_tiles)), dim3(256), 0,
-                     stream, a);
   return hipGetLastError();
 }
 
