@@ -86,7 +86,8 @@ __device__ inline SeqView seq_view(const FwdArgs& a, int b, int h, int D, int es
   return s;
 }
 
-// Backward pass: one launch of each of three kernels (delta, dq, dk/dv).
+// Backward pass: one launch of the dq kernel (which also forms delta), then of the dk/dv kernel
+// (and, when query heads are split, of the reduce kernel).
 struct BwdArgs {
   const void* q;
   const void* k;
