@@ -159,3 +159,27 @@ def test_bwd_rows_past_the_end_are_not_read(case, dtype):
     torch.cuda.synchronize()
     ref = attention_bwd_fp64(decode(q), decode(k), decode(v), decode(do), scale, causal, window)
     check((dq.cpu(), dk.cpu(), dv.cpu()), ref, dtype, f"nan tail {case}")
+
+
+@pytest.mark.parametrize("case", [(1, 333, 200, 4, 1, 64, True), (2, 190, 190, 8, 2, 128, True),
+                                  (1, 256, 256, 16, 1, 64, False), (1, 513, 513, 4, 4, 64, False)],
+                         ids=lambda c: "x".join(str(x) for x in c[:6]) + f"-c{int(c[6])}")
+def test_bwd_workspace_contents_do_not_matter(case):
+    """fa_bwd's workspace holds the per-row terms the dq kernel writes and dk/dv reads (and, for
+    split query heads, the partial sums): filled with NaN and with zeros beforehand, and with dq,
+    dk, dv filled with NaN, the results are the same bit for bit."""
+    B, Nq, Nk, Hq, Hkv, D, causal = case
+    q, k, v, do = draw(B, Nq, Nk, Hq, Hkv, D, torch.float16, seed=Nq + Nk)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    out, lse = fa.fwd(qd, kd, vd, causal=causal)
+    res = []
+    for fill in (float("nan"), 0.0):
+        ws = fa.bwd_workspace(qd, kd)
+        ws.fill_(fill)
+        dq, dk, dv = (torch.full_like(t, float("nan")) for t in (qd, kd, vd))
+        assert fa.bwd_raw(qd, kd, vd, out, dod, lse, dq, dk, dv, ws, causal=causal) == 0
+        torch.cuda.synchronize()
+        res.append([t.cpu() for t in (dq, dk, dv)])
+    for a, b in zip(*res):
+        assert torch.isfinite(a.float()).all()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
