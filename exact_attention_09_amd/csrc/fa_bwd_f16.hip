@@ -519,8 +519,8 @@ fa_bwd_dkdv_kernel(BwdArgs a) {
       // Both blocks full: one sequence S/dP(0), S/dP(1), dV/dK(0), dV/dK(1) in which the softmax
       // of block 0 runs beside S/dP(1) and that of block 1 beside dV/dK(0). Operands are read
       // PF products ahead. At D = 128 the kernel runs one wave per SIMD, and this overlap within
-      // the wave measured 8% faster; at D = 64 two waves share each SIMD and overlap each other,
-      // and the sequence (whose registers would no longer allow two waves) measured slower.
+      // the wave measured 8% faster; at D = 64 three waves share each SIMD and overlap each
+      // other, and the sequence (252 registers: two waves per SIMD) measured 6% slower.
       constexpr int NE = 2 * (NS + ND), PF = 2, GS = NS / 8, GD = ND / 8;
       f32x16 sc0, dp0, sc1, dp1;
       uint32_t pk0[8], dsk0[8], pk1[8], dsk1[8];
