@@ -61,6 +61,9 @@ typedef enum fa_status {
   FA_ERR_DESCALE = 8,   /* FA_FP8_E4M3 without descale_qkv                                         */
   FA_ERR_LAUNCH = 9,    /* the kernel launch failed (HIP error; e.g. no device)                    */
   FA_ERR_TOO_LARGE = 10, /* one head's span of q, k, v or out reaches 2^31 bytes                   */
+                         /* (fa_bwd: also dout, dq, dk, dv); the span counts 256 rows past the    */
+                         /* head's last row, which a ragged tile's 32-bit offsets may address:    */
+                         /* ((rows + 256) * row_stride + D) * element bytes < 2^31                */
   FA_ERR_WORKSPACE = 11, /* fa_bwd / fa_fwd_kvcache: workspace_bytes below what the sizes need     */
   FA_ERR_SCRATCH = 12    /* fa_fwd_kvcache_noalloc: the sizes need more than FA_NOALLOC_SCRATCH_BYTES */
 } fa_status;

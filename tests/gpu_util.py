@@ -101,3 +101,11 @@ def nan_tailed(x, extra=128, device="cuda"):
     big = torch.full((B, N + extra, H, D), float("nan"), dtype=x.dtype, device=device)
     big[:, :N] = x.to(device)
     return big[:, :N]
+
+
+def widest_row_stride(rows: int, D: int, elem_bytes: int) -> int:
+    """The largest row stride (in elements, a whole number of 16-byte units) for which a head of
+    ``rows`` rows passes the library's span rule, ((rows + 256) * stride + D) * elem_bytes < 2^31
+    (include/fa355.h, FA_ERR_TOO_LARGE); one 16-byte unit more is rejected."""
+    s = ((1 << 31) - 1 - D * elem_bytes) // ((rows + 256) * elem_bytes)
+    return s - s % (16 // elem_bytes)

@@ -11,6 +11,7 @@ import pytest
 
 import exact_attention_09_amd as fa
 from exact_attention_09_amd.fa355 import FaStrides
+from tests.gpu_util import widest_row_stride
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fa355.h")
@@ -104,6 +105,22 @@ def test_rejects_too_large(lib):
     # one head of k spans more than 2^31 bytes
     s = FaStrides(0, 64, 64, 0, 1 << 20, 64, 0, 64, 64, 0, 64, 64)
     assert call(lib, B=1, Nq=1, Nk=2048, Hq=1, Hkv=1, strides=s) == 10
+
+
+@pytest.mark.parametrize("dtype,D,rows", [(0, 64, 2047), (1, 128, 1999), (2, 64, 2047), (2, 128, 1)])
+@pytest.mark.parametrize("which", ["q", "k", "v", "o"])
+def test_rejects_one_unit_past_the_widest_span(lib, dtype, D, rows, which):
+    # the widest stride of widest_row_stride is the one the GPU max-span tests run; one 16-byte
+    # unit more in any one tensor's row stride must be refused before any launch
+    es = 1 if dtype == 2 else 2
+    es_of = {"q": es, "k": es, "v": es, "o": 2}
+    st = {}
+    for t in "qkvo":
+        st[t] = widest_row_stride(rows, D, es_of[t])
+    st[which] += 16 // es_of[which]
+    s = FaStrides(0, st["q"], D, 0, st["k"], D, 0, st["v"], D, 0, st["o"], D)
+    desc = (1.0, 1.0, 1.0) if dtype == 2 else None
+    assert call(lib, B=1, Nq=rows, Nk=rows, Hq=1, Hkv=1, D=D, strides=s, dtype=dtype, descale=desc) == 10
 
 
 # --- K/V tile planning vs brute-force admission --------------------------------------------
