@@ -6,16 +6,17 @@ Each tensor is a strided view of a large device buffer: its rows sit the widest 
 apart (a head of 2047 fp16 rows then spans about 1.9 GB), so the kernels' 32-bit in-head offsets
 reach their top, and each batch starts more than 2^31 bytes after the one before (batch offsets
 are 64-bit). Results must match the fp64 oracle at the usual bars; outputs start NaN-filled, so a
-row written nowhere fails. Each case needs 8-35 GB of device memory and none of the host's beyond
-the small inputs.
+row written nowhere fails. The KV-cache calls, which address each key in 64 bits and have no
+span limit, run with used pages past 4 GiB and sequences more than 2 GiB apart. Each case needs
+8-35 GB of device memory and none of the host's beyond the small inputs.
 """
 import numpy as np
 import pytest
 import torch
 
 import exact_attention_09_amd as fa
-from exact_attention_09_amd.inputs import draw_qkv, make_varlen_inputs, to_storage
-from oracle import attention_bwd_fp64, attention_varlen_fp64
+from exact_attention_09_amd.inputs import draw_qkv, make_kvcache_inputs, make_varlen_inputs, to_storage
+from oracle import attention_bwd_fp64, attention_kvcache_fp64, attention_varlen_fp64
 from tests.gpu_util import DTYPE_NAME, compare, decode, oracle_full, out_to_f64, widest_row_stride
 from tests.test_gpu_bwd import check as bwd_check
 from tests.test_gpu_bwd import draw as bwd_draw
@@ -126,3 +127,38 @@ def test_varlen_widest_spans():
     ro, rl = attention_varlen_fp64(decode(q), decode(k), decode(v), cu_q.numpy(), cu_k.numpy(), scale, True,
                                    (-1, -1))
     compare("f16", out_to_f64(ow.cpu()), lse.cpu().numpy().astype(np.float64), ro, rl, "varlen widest spans")
+
+
+def test_kvcache_pages_past_4_gib():
+    # a paged cache of about 4.3 GB per tensor whose used pages sit at its top: page byte offsets
+    # above 2^32 (the decode kernel forms each key's address in 64 bits)
+    B, Nq, Hq, Hkv, D, lens, P = 3, 2, 8, 2, 128, [1000, 4100, 17], 16
+    q, k, v, seqlens, table = make_kvcache_inputs(B, Nq, Hq, Hkv, D, "bf16", lens, P, seed=5)
+    base = (1 << 32) // (P * Hkv * D * 2) + 1000
+    kc = torch.empty(base + k.shape[0], P, Hkv, D, dtype=k.dtype, device="cuda")
+    vc = torch.empty_like(kc)
+    kc[base:] = k.cuda()
+    vc[base:] = v.cuda()
+    scale = D ** -0.5
+    out, lse = fa.fwd_kvcache(q.cuda(), kc, vc, seqlens.cuda(), (table + base).to(torch.int32).cuda(), max(lens),
+                              True, (-1, -1), scale)
+    torch.cuda.synchronize()
+    ro, rl = attention_kvcache_fp64(decode(q), decode(k), decode(v), lens, table.numpy(), P, scale, True, (-1, -1))
+    compare("bf16", out_to_f64(out.cpu()), lse.cpu().numpy().astype(np.float64), ro, rl, "paged cache past 4 GiB")
+
+
+def test_kvcache_dense_batches_past_2_gib():
+    # a dense cache whose second sequence starts more than 2^31 bytes after the first
+    B, Nq, Hq, Hkv, D, lens = 2, 3, 8, 2, 128, [3000, 2500]
+    q, k, v, seqlens, _ = make_kvcache_inputs(B, Nq, Hq, Hkv, D, "f16", lens, 0, seed=6)
+    rows = (1 << 31) // (Hkv * D * 2) + 64
+    kc = torch.empty(B, rows, Hkv, D, dtype=k.dtype, device="cuda")
+    vc = torch.empty_like(kc)
+    kc[:, :k.shape[1]] = k.cuda()
+    vc[:, :v.shape[1]] = v.cuda()
+    assert kc.stride(0) * kc.element_size() > 1 << 31
+    scale = D ** -0.5
+    out, lse = fa.fwd_kvcache(q.cuda(), kc, vc, seqlens.cuda(), None, max(lens), True, (-1, -1), scale)
+    torch.cuda.synchronize()
+    ro, rl = attention_kvcache_fp64(decode(q), decode(k), decode(v), lens, None, 0, scale, True, (-1, -1))
+    compare("f16", out_to_f64(out.cpu()), lse.cpu().numpy().astype(np.float64), ro, rl, "dense cache past 2 GiB")
