@@ -31,6 +31,13 @@ import oracle.attention as OA
 import oracle.formats as OF
 from oracle import admitted, attention_fp64, decode_bf16_bits, decode_e4m3_codes, decode_f16_bits, tiled_online_fp64
 
+
+def nanmax(*xs):
+    """max that keeps a NaN (Python's max drops one that is not its first argument), so a pin
+    whose oracle result turns NaN fails instead of passing."""
+    return float(np.max(np.array(xs, dtype=np.float64)))
+
+
 GOLDEN_GRID = __file__.rsplit("/", 1)[0] + "/golden/grid_8x8_2x2.txt"
 
 
@@ -76,7 +83,9 @@ def sdpa_reference(q, k, v, scale, causal, window):
 
 def read_grid(path=GOLDEN_GRID):
     meta, grid, inside = {}, [], False
-    for line in open(path):
+    with open(path) as f:
+        lines = f.read().splitlines()
+    for line in lines:
         line = line.strip()
         if not line or line.startswith("#"):
             continue
@@ -116,7 +125,7 @@ def pin_sdpa():
         scale = 1.0 / math.sqrt(D) * (1.3 if seed % 2 else 1.0)
         o, l = attention_fp64(q, k, v, scale, causal, window)
         ro, rl = sdpa_reference(q, k, v, scale, causal, window)
-        worst = max(worst, np.abs(o - ro).max(), np.abs(l - rl).max())
+        worst = nanmax(worst, np.abs(o - ro).max(), np.abs(l - rl).max())
     return worst
 
 
@@ -149,8 +158,8 @@ def pin_bruteforce():
                 z = mpmath.fsum(mpmath.exp(s[j]) for j in keys)
                 for d in range(D):
                     ref = mpmath.fsum(mpmath.exp(s[j]) * mpmath.mpf(v[0, j, g, d]) for j in keys) / z
-                    worst = max(worst, abs(float(ref) - o[0, i, h, d]))
-                worst = max(worst, abs(float(mpmath.log(z)) - l[0, h, i]))
+                    worst = nanmax(worst, abs(float(ref) - o[0, i, h, d]))
+                worst = nanmax(worst, abs(float(mpmath.log(z)) - l[0, h, i]))
     return worst
 
 
@@ -167,7 +176,7 @@ def pin_grid_example():
             q, k, v = rand_qkv(200 + seed, 1, n, n, 1, 1, 4)
             o, l = attention_fp64(q, k, v, 0.5, causal)
             to, tl, classes = tiled_online_fp64(q, k, v, 0.5, causal, block_q=br, block_k=bc)
-            worst = max(worst, np.abs(o - to).max(), np.abs(l - tl).max())
+            worst = nanmax(worst, np.abs(o - to).max(), np.abs(l - tl).max())
             if causal:
                 got = (classes["skipped"], classes["partial"], classes["full"])
                 want = (meta["causal_skipped"], meta["causal_partial"], meta["causal_full"])
@@ -188,7 +197,7 @@ def pin_grid_example():
         to, tl, _ = tiled_online_fp64(q, k, v, 0.4, causal, win, block_q=int(g.integers(1, 7)),
                                       block_k=int(g.integers(1, 7)))
         fin = np.isfinite(l)
-        worst = max(worst, np.abs(o - to).max(), np.abs(l[fin] - tl[fin]).max())
+        worst = nanmax(worst, np.abs(o - to).max(), np.abs(l[fin] - tl[fin]).max())
         if not np.array_equal(np.isfinite(l), np.isfinite(tl)):
             return math.inf
     return worst
@@ -205,7 +214,7 @@ def pin_row_shift():
         o2, l2 = attention_fp64(q, k + u, v, scale, causal, win)
         G = 2
         c = scale * np.einsum("bihd,d->bhi", q, u)
-        worst = max(worst, np.abs(o - o2).max(), np.abs((l2 - l) - c).max())
+        worst = nanmax(worst, np.abs(o - o2).max(), np.abs((l2 - l) - c).max())
     return worst
 
 
@@ -214,8 +223,8 @@ def pin_causal_row0():
     o, l = attention_fp64(q, k, v, 0.3, True)
     worst = 0.0
     for h in range(4):
-        worst = max(worst, np.abs(o[:, 0, h, :] - v[:, 0, h // 2, :]).max())
-        worst = max(worst, np.abs(l[:, h, 0] - 0.3 * np.sum(q[:, 0, h, :] * k[:, 0, h // 2, :], -1)).max())
+        worst = nanmax(worst, np.abs(o[:, 0, h, :] - v[:, 0, h // 2, :]).max())
+        worst = nanmax(worst, np.abs(l[:, h, 0] - 0.3 * np.sum(q[:, 0, h, :] * k[:, 0, h // 2, :], -1)).max())
     return worst
 
 
@@ -232,8 +241,8 @@ def pin_identical_keys():
             mean = v[0, lo:hi + 1, 0, :].mean(0)
             cnt = hi - lo + 1
             for h in range(2):
-                worst = max(worst, np.abs(o[0, i, h] - mean).max())
-                worst = max(worst, abs(l[0, h, i] - (0.7 * q[0, i, h] @ k[0, 0, 0] + math.log(cnt))))
+                worst = nanmax(worst, np.abs(o[0, i, h] - mean).max())
+                worst = nanmax(worst, abs(l[0, h, i] - (0.7 * q[0, i, h] @ k[0, 0, 0] + math.log(cnt))))
     return worst
 
 
@@ -251,7 +260,7 @@ def pin_big_window():
         o, l = attention_fp64(q, k, v, 0.5, causal)
         for win in ((13, 13), (40, 99), (12, 12)):
             o2, l2 = attention_fp64(q, k, v, 0.5, causal, win)
-            worst = max(worst, np.abs(o - o2).max(), np.abs(l - l2).max())
+            worst = nanmax(worst, np.abs(o - o2).max(), np.abs(l - l2).max())
     return worst
 
 
@@ -283,7 +292,7 @@ def pin_mask_probe():
             have = np.rint(o[0, i, 0] * cnt[i]) if cnt[i] else np.zeros(D)
             if not np.array_equal(have, want):
                 return math.inf
-            worst = max(worst, np.abs(o[0, i, 0] * cnt[i] - want).max())
+            worst = nanmax(worst, np.abs(o[0, i, 0] * cnt[i] - want).max())
     return worst
 
 
