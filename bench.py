@@ -333,10 +333,10 @@ def main():
     if not bwd and args.workload == DEFAULT_WORKLOAD and args.bars:
         # the other configurations the throughput bars are stated on, measured in the same run
         rec["bars"] = {}
-        for name in BAR_WORKLOADS:
-            r = bench_dense(args, WORKLOADS[name], dev, False, cold_launches=0, cpu_seconds=0)
+        for name, bar_bwd in BAR_WORKLOADS:
+            r = bench_dense(args, WORKLOADS[name], dev, bar_bwd, cold_launches=0, cpu_seconds=0)
             rf = r["roofline"]
-            rec["bars"][name] = {
+            rec["bars"][name + ("_bwd" if bar_bwd else "")] = {
                 "dtype": r["dtype"], "ms_per_step": r["ms_per_step"], "TFLOPs": r["value"],
                 "pct_of_mfma_peak": r["pct_of_mfma_peak"], "kernel_avg_us": rf["kernel_avg_us"],
                 "roofline": {key: rf[key] for key in ("bound", "achieved", "peak", "unit", "frac", "traffic")},
@@ -344,10 +344,13 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-# Configurations of the throughput bars measured beside the default workload: the same shape in
-# bf16, the fp8 workload, and the long GQA workload (causal, and with the (256, 256) window).
-BAR_WORKLOADS = ["causal_b4_h32_n4096_d64_bf16", "causal_fp8_b2_h32_n4096_d64_e4m3",
-                 "gqa_b1_hq32_hkv8_n16384_d128_bf16", "gqa_win256_b1_hq32_hkv8_n16384_d128_bf16"]
+# Configurations measured beside the default workload, as (workload, backward?): the same shape in
+# bf16, the fp8 workload, the long GQA and MQA workloads (causal, and with the (256, 256) window),
+# and the backward pass of the default workload (keyed with a "_bwd" suffix).
+BAR_WORKLOADS = [("causal_b4_h32_n4096_d64_bf16", False), ("causal_fp8_b2_h32_n4096_d64_e4m3", False),
+                 ("gqa_b1_hq32_hkv8_n16384_d128_bf16", False), ("gqa_win256_b1_hq32_hkv8_n16384_d128_bf16", False),
+                 ("mqa_b1_hq32_hkv1_n16384_d128_bf16", False), ("mqa_win256_b1_hq32_hkv1_n16384_d128_bf16", False),
+                 ("causal_b4_h32_n4096_d64_f16", True)]
 
 
 def bench_dense(args, w, dev, bwd, cold_launches=0, cpu_seconds=0.0):
