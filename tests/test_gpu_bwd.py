@@ -183,3 +183,31 @@ def test_bwd_workspace_contents_do_not_matter(case):
     for a, b in zip(*res):
         assert torch.isfinite(a.float()).all()
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_bwd_c3_every_head_equals_single_head_launches():
+    """Every element of the causal [4, 4096, 32, 64] fp16 backward: the full launch (its launch
+    order, chunked by heads over the XCDs) against 128 launches of one (batch, head) each, which
+    take the single-head order. Each workgroup's arithmetic does not depend on where the launch
+    order puts it (no atomics, no split at Hq = Hkv), so the two must agree bit for bit; a tile
+    that the full order skipped or computed twice would not. Single-head launches are held to the
+    oracle by the other tests (one c3 head above in full)."""
+    B, N, H, D = 4, 4096, 32, 64
+    q, k, v, do = draw(B, N, N, H, H, D, torch.float16, seed=3)
+    qd, kd, vd, dod = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    out, lse = fa.fwd(qd, kd, vd, causal=True)
+    full = [torch.full_like(qd, float("nan")) for _ in range(3)]
+    st = fa.bwd_raw(qd, kd, vd, out, dod, lse, *full, fa.bwd_workspace(qd, kd), causal=True)
+    assert st == 0, fa.status_str(st)
+    ws1 = fa.bwd_workspace(qd[:1, :, :1], kd[:1, :, :1])
+    sl = lambda t, b, h: t[b:b + 1, :, h:h + 1, :]
+    one = [torch.empty(1, N, 1, D, dtype=torch.float16, device="cuda") for _ in range(3)]
+    for b in range(B):
+        for h in range(H):
+            for t in one:
+                t.fill_(float("nan"))
+            st = fa.bwd_raw(sl(qd, b, h), sl(kd, b, h), sl(vd, b, h), sl(out, b, h), sl(dod, b, h),
+                            lse[b:b + 1, h:h + 1], *one, ws1, causal=True)
+            assert st == 0, fa.status_str(st)
+            for name, f, o in zip(("dq", "dk", "dv"), full, one):
+                assert torch.equal(sl(f, b, h).view(torch.int16), o.view(torch.int16)), f"{name} of ({b}, {h})"
