@@ -178,6 +178,31 @@ def test_full_size_every_head_sampled_rows(name):
                 what=f"{name} b{b} h{h}")
 
 
+
+@pytest.mark.parametrize("name", FULL_SAMPLED)
+def test_full_size_every_element_equals_per_group_launches(name):
+    """Every element of the [1, 16384, 32, 128] GQA / MQA launches (causal, and with the window):
+    the full launch, in its chunked XCD order, against eight launches of one group of four query
+    heads each (with their K/V head), which take the single-group order. No workgroup's arithmetic
+    depends on where the launch order puts it, so the two agree bit for bit unless the full order
+    skips a tile or computes one twice; the oracle holds every head on sampled rows (above)."""
+    w = WORKLOADS[name]
+    q, k, v, d = make_inputs(w, w.seeds[0])
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    odt = torch.float16 if w.dtype == "f16" else torch.bfloat16
+    out, lse = nan_outputs(w.B, w.Nq, w.Hq, w.D, odt)
+    fa.fwd(qd, kd, vd, w.causal, w.window, w.softmax_scale(), d, out=out, lse=lse)
+    G = 4
+    for g in range(w.Hq // G):
+        kv = g * G * w.Hkv // w.Hq
+        o1, l1 = nan_outputs(w.B, w.Nq, G, w.D, odt)
+        fa.fwd(qd[:, :, g * G:(g + 1) * G], kd[:, :, kv:kv + 1], vd[:, :, kv:kv + 1], w.causal, w.window,
+               w.softmax_scale(), d, out=o1, lse=l1)
+        torch.cuda.synchronize()
+        assert torch.equal(out[:, :, g * G:(g + 1) * G].view(torch.int16), o1.view(torch.int16)), f"out of group {g}"
+        assert torch.equal(lse[:, g * G:(g + 1) * G], l1), f"lse of group {g}"
+
+
 # ---------------------------------------------------------------- masks, exactly
 def probe_inputs(B, Nq, Nk, Hq, Hkv, D, tdt, mode):
     q = torch.zeros(B, Nq, Hq, D, dtype=tdt)
