@@ -114,3 +114,30 @@ def test_varlen_benchmark_workload_sampled(name):
             got_o = out_to_f64(out[s:s + n, h])[rows]
             got_l = lse[h, s:s + n].numpy().astype(np.float64)[rows]
             compare(w.dtype, got_o, got_l, ro, rl, f"{name} seq {b} head {h}")
+
+
+@pytest.mark.parametrize("name", list(VARLEN_WORKLOADS))
+def test_varlen_benchmark_workload_every_element_equals_dense(name):
+    """Every element of the benchmark's packed batches, in the launch it times, against one dense
+    launch per sequence (its rows of the packed tensors as a [1, n, H, D] view), bit for bit: a
+    packed sequence is the dense problem of its own lengths with the same tiles and arithmetic
+    (reading RV1), so only a tile that the packed launch order skipped or computed twice, or a
+    sequence offset gone wrong, would differ. The dense launches are held to the oracle by the
+    dense tests; the packed one on sampled rows above."""
+    w = VARLEN_WORKLOADS[name]
+    lens = w.lengths(0)
+    q, k, v, cu_q, cu_k, d = make_varlen_inputs(lens, lens, w.Hq, w.Hkv, w.D, w.dtype, seed=0)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    odt = torch.float16 if w.dtype == "f16" else torch.bfloat16
+    out = torch.full(q.shape, float("nan"), dtype=odt, device="cuda")
+    lse = torch.full((w.Hq, q.shape[0]), float("nan"), dtype=torch.float32, device="cuda")
+    st = fa.fwd_varlen_raw(qd, kd, vd, out, lse, cu_q.cuda(), cu_k.cuda(), max(lens), w.causal, w.window,
+                           w.softmax_scale(), d)
+    assert st == 0, fa.status_str(st)
+    for b, n in enumerate(lens):
+        s = int(cu_q[b])
+        do, dl = fa.fwd(qd[s:s + n].unsqueeze(0), kd[s:s + n].unsqueeze(0), vd[s:s + n].unsqueeze(0), w.causal,
+                        w.window, w.softmax_scale(), d)
+        torch.cuda.synchronize()
+        assert torch.equal(out[s:s + n].view(torch.int16), do[0].view(torch.int16)), f"out of sequence {b}"
+        assert torch.equal(lse[:, s:s + n], dl[0]), f"lse of sequence {b}"
