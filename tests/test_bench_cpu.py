@@ -113,3 +113,17 @@ def test_roofline_bound_of_the_workloads():
     assert bench.roofline_bound(bench.metric_flops(w), 337641472, 2516.6) == "hbm"
     assert bench.roofline_bound(bench.metric_flops(w), 337641472, 1e9) == "hbm"
     assert bench.roofline_bound(bench.metric_flops(w), 1, 2516.6) == "mfma"
+
+
+def test_bar_workloads_cover_every_bar_configuration():
+    """The default line's `bars`: each entry names a dense workload; the backward entry takes fp16 or
+    bf16; together with the default workload they cover both dtypes of the 4096-token causal
+    shape, the fp8 run, and the GQA and MQA runs with and without the window."""
+    names = [n for n, _ in bench.BAR_WORKLOADS]
+    assert all(n in WORKLOADS for n in names)
+    assert all(WORKLOADS[n].dtype != "e4m3" for n, bwd in bench.BAR_WORKLOADS if bwd)
+    covered = set(names) | {bench.DEFAULT_WORKLOAD}
+    assert {"causal_b4_h32_n4096_d64_f16", "causal_b4_h32_n4096_d64_bf16", "causal_fp8_b2_h32_n4096_d64_e4m3",
+            "gqa_b1_hq32_hkv8_n16384_d128_bf16", "mqa_b1_hq32_hkv1_n16384_d128_bf16",
+            "gqa_win256_b1_hq32_hkv8_n16384_d128_bf16", "mqa_win256_b1_hq32_hkv1_n16384_d128_bf16"} <= covered
+    assert len({(n, b) for n, b in bench.BAR_WORKLOADS}) == len(bench.BAR_WORKLOADS)
