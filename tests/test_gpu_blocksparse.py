@@ -103,3 +103,27 @@ def test_blocksparse_benchmark_workload_sampled(name):
                 o1, l1 = attention_rows_fp64(qh[:, i:i + 1], kh[:, keys], vh[:, keys], 0, 0, [0], w.softmax_scale())
                 ro[n], rl[n] = o1[0], l1[0]
         compare(w.dtype, out_to_f64(out[0, rows, h]), lse[0, h, rows].numpy().astype(np.float64), ro, rl, f"{name} h{h}")
+
+
+@pytest.mark.parametrize("name", list(SPARSE_WORKLOADS))
+def test_blocksparse_benchmark_every_element_equals_single_head_launches(name):
+    """Every element of the benchmark's sparse launches against one launch per query head (its
+    q, K/V head and mask row as views), bit for bit: each workgroup builds the same tile list from
+    the same mask row and runs the same arithmetic wherever the launch order puts it, so only a
+    tile the full launch skipped or computed twice, or a mask row read for the wrong head, would
+    differ. The sampled rows above hold the full launch to the oracle."""
+    w = SPARSE_WORKLOADS[name]
+    q, k, v = draw_qkv(w.B, w.N, w.N, w.Hq, w.Hkv, w.D, seed=0)
+    q, k, v, _ = to_storage(q, k, v, w.dtype)
+    mask = w.mask(0).cuda()
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    out, lse = fa.fwd_blocksparse(qd, kd, vd, mask, w.causal, (-1, -1), w.softmax_scale())
+    G = w.Hq // w.Hkv
+    for h in range(w.Hq):
+        g = h // G
+        mh = mask[0:1] if mask.shape[0] == 1 else mask[h:h + 1]
+        o1, l1 = fa.fwd_blocksparse(qd[:, :, h:h + 1], kd[:, :, g:g + 1], vd[:, :, g:g + 1], mh, w.causal, (-1, -1),
+                                    w.softmax_scale())
+        torch.cuda.synchronize()
+        assert torch.equal(out[:, :, h:h + 1].view(torch.int16), o1.view(torch.int16)), f"out of head {h}"
+        assert torch.equal(lse[:, h:h + 1], l1), f"lse of head {h}"
